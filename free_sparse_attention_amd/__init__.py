@@ -1,0 +1,25 @@
+"""Combined sparse decode attention for MI355X (gfx950).
+
+The computation lives in ``libfsa.so`` (HIP kernels behind the C ABI of
+``include/fsa.h``); this package is its thin ctypes binding plus the build
+script.  PyTorch is used only for device memory and streams.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    Dims,
+    FsaError,
+    LayerCfg,
+    append_kv,
+    build_page_meta,
+    cfg,
+    dense_decode_attn,
+    dense_decode_workspace_bytes,
+    dims,
+    import_kv_plain,
+    load,
+    max_work_items,
+    quest_scores,
+    select_pages,
+    sparse_decode_attn,
+    sparse_decode_workspace_bytes,
+)

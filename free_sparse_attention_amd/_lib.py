@@ -1,0 +1,187 @@
+"""ctypes binding of libfsa.so (include/fsa.h).
+
+Argument marshalling only: torch tensors are passed as raw device pointers and
+the current torch stream as the HIP stream; every step of the computation
+runs in the library's kernels.  There is no fallback: if libfsa.so is missing
+or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfsa.so")
+
+FSA_OK, FSA_ERR_INVALID_ARG, FSA_ERR_UNSUPPORTED, FSA_ERR_WORKSPACE, FSA_ERR_HIP = range(5)
+
+EXPORTED = (
+    "fsa_last_error", "fsa_import_kv_plain", "fsa_append_kv", "fsa_build_page_meta",
+    "fsa_quest_scores", "fsa_max_work_items", "fsa_select_pages",
+    "fsa_sparse_decode_workspace_bytes", "fsa_sparse_decode_attn",
+    "fsa_dense_decode_workspace_bytes", "fsa_dense_decode_attn",
+)
+
+
+class FsaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"fsa status {status}: {msg}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+                ("num_pool_pages", ctypes.c_int32)]
+
+
+class LayerCfg(ctypes.Structure):
+    _fields_ = [("prefix_tokens", ctypes.c_int32), ("window_tokens", ctypes.c_int32),
+                ("budget_pages", ctypes.c_int32)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfsa.so and declare its signatures (raises if it is not built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m free_sparse_attention_amd.build`")
+        L = ctypes.CDLL(path)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+        D, C = ctypes.POINTER(Dims), LayerCfg
+        sig = {
+            "fsa_last_error": (ctypes.c_char_p, []),
+            "fsa_import_kv_plain": (i32, [D, vp, vp, vp, vp, vp]),
+            "fsa_append_kv": (i32, [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+            "fsa_build_page_meta": (i32, [D, vp, vp, vp, vp, vp]),
+            "fsa_quest_scores": (i32, [D, C, i32, vp, vp, vp, vp, vp, vp]),
+            "fsa_max_work_items": (i32, [D, C, i32]),
+            "fsa_select_pages": (i32, [D, C, i32, vp, vp, vp, vp, vp, vp, vp]),
+            "fsa_sparse_decode_workspace_bytes": (sz, [D, C, i32]),
+            "fsa_sparse_decode_attn": (i32, [D, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "fsa_dense_decode_workspace_bytes": (sz, [D, i32]),
+            "fsa_dense_decode_attn": (i32, [D, f32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+        return L
+
+
+def _check(status: int) -> None:
+    if status != FSA_OK:
+        raise FsaError(status, load().fsa_last_error().decode())
+
+
+def _p(t: torch.Tensor | None, name: str, dtype_size: int | None = None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype_size is not None and t.element_size() != dtype_size:
+        raise ValueError(f"{name}: element size {t.element_size()}, expected {dtype_size}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _i32(t, name):
+    if t is not None and t.dtype != torch.int32:
+        raise ValueError(f"{name} must be int32")
+    return _p(t, name)
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def dims(batch, num_q_heads, num_kv_heads, head_dim, max_pages_per_seq, num_pool_pages, page_size=16) -> Dims:
+    return Dims(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq, num_pool_pages)
+
+
+def cfg(prefix_tokens, window_tokens, budget_pages) -> LayerCfg:
+    return LayerCfg(prefix_tokens, window_tokens, budget_pages)
+
+
+def import_kv_plain(d: Dims, k_plain, v_plain, k_cache, v_cache, stream=None):
+    _check(load().fsa_import_kv_plain(ctypes.byref(d), _p(k_plain, "k_plain", 2), _p(v_plain, "v_plain", 2),
+                                      _p(k_cache, "k_cache", 2), _p(v_cache, "v_cache", 2), _stream(stream)))
+
+
+def append_kv(d: Dims, n_new, k_new, v_new, page_table, seq_lens, seq_lens_out, k_cache, v_cache, meta,
+              stream=None):
+    _check(load().fsa_append_kv(ctypes.byref(d), int(n_new), _p(k_new, "k_new", 2), _p(v_new, "v_new", 2),
+                                _i32(page_table, "page_table"), _i32(seq_lens, "seq_lens"),
+                                _i32(seq_lens_out, "seq_lens_out"), _p(k_cache, "k_cache", 2),
+                                _p(v_cache, "v_cache", 2), _p(meta, "meta", 2), _stream(stream)))
+
+
+def build_page_meta(d: Dims, k_cache, page_table, seq_lens, meta, stream=None):
+    _check(load().fsa_build_page_meta(ctypes.byref(d), _p(k_cache, "k_cache", 2), _i32(page_table, "page_table"),
+                                      _i32(seq_lens, "seq_lens"), _p(meta, "meta", 2), _stream(stream)))
+
+
+def quest_scores(d: Dims, c: LayerCfg, max_seq_len, q, meta, page_table, seq_lens, scores, stream=None):
+    _check(load().fsa_quest_scores(ctypes.byref(d), c, int(max_seq_len), _p(q, "q", 2), _p(meta, "meta", 2),
+                                   _i32(page_table, "page_table"), _i32(seq_lens, "seq_lens"),
+                                   _p(scores, "scores", 4), _stream(stream)))
+
+
+def max_work_items(d: Dims, c: LayerCfg, max_seq_len) -> int:
+    n = load().fsa_max_work_items(ctypes.byref(d), c, int(max_seq_len))
+    if n < 0:
+        raise FsaError(FSA_ERR_INVALID_ARG, load().fsa_last_error().decode())
+    return n
+
+
+def select_pages(d: Dims, c: LayerCfg, max_seq_len, scores, page_table, seq_lens, sel_pages=None, work=None,
+                 counts=None, stream=None):
+    _check(load().fsa_select_pages(ctypes.byref(d), c, int(max_seq_len), _p(scores, "scores", 4),
+                                   _i32(page_table, "page_table"), _i32(seq_lens, "seq_lens"),
+                                   _i32(sel_pages, "sel_pages"), _i32(work, "work"), _i32(counts, "counts"),
+                                   _stream(stream)))
+
+
+def sparse_decode_workspace_bytes(d: Dims, c: LayerCfg, max_seq_len) -> int:
+    n = load().fsa_sparse_decode_workspace_bytes(ctypes.byref(d), c, int(max_seq_len))
+    if n == 0:
+        raise FsaError(FSA_ERR_INVALID_ARG, load().fsa_last_error().decode())
+    return n
+
+
+def sparse_decode_attn(d: Dims, c: LayerCfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table,
+                       seq_lens, out, sel_pages, workspace, stream=None):
+    _check(load().fsa_sparse_decode_attn(
+        ctypes.byref(d), c, float(sm_scale), int(max_seq_len), _p(q, "q", 2), _p(k_cache, "k_cache", 2),
+        _p(v_cache, "v_cache", 2), _p(meta, "meta", 2), _i32(page_table, "page_table"),
+        _i32(seq_lens, "seq_lens"), _p(out, "out", 2), _i32(sel_pages, "sel_pages"),
+        _p(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def dense_decode_workspace_bytes(d: Dims, max_seq_len) -> int:
+    n = load().fsa_dense_decode_workspace_bytes(ctypes.byref(d), int(max_seq_len))
+    if n == 0:
+        raise FsaError(FSA_ERR_INVALID_ARG, load().fsa_last_error().decode())
+    return n
+
+
+def dense_decode_attn(d: Dims, sm_scale, max_seq_len, q, k_cache, v_cache, page_table, seq_lens, out,
+                      workspace, stream=None):
+    _check(load().fsa_dense_decode_attn(
+        ctypes.byref(d), float(sm_scale), int(max_seq_len), _p(q, "q", 2), _p(k_cache, "k_cache", 2),
+        _p(v_cache, "v_cache", 2), _i32(page_table, "page_table"), _i32(seq_lens, "seq_lens"),
+        _p(out, "out", 2), _p(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))

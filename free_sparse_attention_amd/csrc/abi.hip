@@ -1,0 +1,331 @@
+// C-ABI entry points declared in include/fsa.h: host-side argument checks,
+// workspace layout and launch sequencing on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "../../include/fsa.h"
+#include "fsa_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+fsa_status fail(fsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+fsa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return FSA_OK;
+  return fail(FSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define FSA_CHECK(expr)              \
+  do {                               \
+    const fsa_status _s = (expr);    \
+    if (_s != FSA_OK) return _s;     \
+  } while (0)
+
+fsa_status check_dims(const fsa_dims* d) {
+  if (!d) return fail(FSA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->batch < 1 || d->num_kv_heads < 1 || d->num_q_heads < 1 || d->max_pages_per_seq < 1 ||
+      d->num_pool_pages < 1)
+    return fail(FSA_ERR_INVALID_ARG, "dims: batch, heads, max_pages_per_seq and num_pool_pages must be >= 1");
+  if (d->num_q_heads % d->num_kv_heads != 0)
+    return fail(FSA_ERR_INVALID_ARG, "dims: num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                d->num_q_heads, d->num_kv_heads);
+  if (d->num_q_heads / d->num_kv_heads > 16)
+    return fail(FSA_ERR_UNSUPPORTED, "dims: query group of %d heads; at most 16 are supported",
+                d->num_q_heads / d->num_kv_heads);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(FSA_ERR_UNSUPPORTED, "dims: head_dim %d; supported are 64 and 128", d->head_dim);
+  if (d->page_size != fsa::kPage)
+    return fail(FSA_ERR_UNSUPPORTED, "dims: page_size %d; supported is 16", d->page_size);
+  if ((long long)d->batch * d->max_pages_per_seq > (1LL << 31) ||
+      (long long)d->num_pool_pages * d->num_kv_heads > (1LL << 31))
+    return fail(FSA_ERR_UNSUPPORTED, "dims: page table or pool too large");
+  return FSA_OK;
+}
+
+fsa_status check_cfg(fsa_layer_cfg c) {
+  if (c.prefix_tokens < 0 || c.window_tokens < 0 || c.budget_pages < 0)
+    return fail(FSA_ERR_INVALID_ARG, "cfg: prefix, window and budget must be >= 0");
+  if (c.prefix_tokens == 0 && c.window_tokens == 0 && c.budget_pages == 0)
+    return fail(FSA_ERR_INVALID_ARG, "cfg: prefix = window = budget = 0 attends to nothing");
+  return FSA_OK;
+}
+
+fsa_status check_len(const fsa_dims* d, int32_t max_seq_len) {
+  if (max_seq_len < 1 || (long long)max_seq_len > (long long)d->max_pages_per_seq * d->page_size)
+    return fail(FSA_ERR_INVALID_ARG, "max_seq_len %d outside [1, max_pages_per_seq * page_size]",
+                max_seq_len);
+  return FSA_OK;
+}
+
+fsa_status need(const void* p, const char* name) {
+  if (!p) return fail(FSA_ERR_INVALID_ARG, "%s is NULL", name);
+  return FSA_OK;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int n_pages_max(int32_t max_seq_len) { return (max_seq_len + fsa::kPage - 1) / fsa::kPage; }
+
+int max_items_of(const fsa_dims* d, fsa_layer_cfg c, int32_t max_seq_len) {
+  const long n = n_pages_max(max_seq_len);
+  const long pre = std::min<long>((c.prefix_tokens + fsa::kPage - 1) / fsa::kPage, n);
+  const long sel = std::min<long>(c.budget_pages, n);
+  const long win = std::min<long>((c.window_tokens + fsa::kPage - 1) / fsa::kPage + 1, n);
+  (void)d;
+  return (int)std::max<long>(1, pre + sel + win);
+}
+
+// Workspace of the sparse step: [scores][work][counts][counters][part_ml][part_o]
+struct SparseWs {
+  size_t scores, work, counts, counters, part_ml, part_o, total;
+  int max_items;
+  fsa::AttnPlan plan;
+};
+
+SparseWs sparse_ws(const fsa_dims* d, fsa_layer_cfg c, int32_t max_seq_len) {
+  SparseWs w;
+  const size_t units = (size_t)d->batch * d->num_kv_heads;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  w.max_items = max_items_of(d, c, max_seq_len);
+  w.plan = fsa::plan_attention((int)units, w.max_items);
+  size_t o = 0;
+  w.scores = o;   o = align256(o + units * d->max_pages_per_seq * sizeof(float));
+  w.work = o;     o = align256(o + units * w.max_items * 4 * sizeof(int32_t));
+  w.counts = o;   o = align256(o + units * 2 * sizeof(int32_t));
+  w.counters = o; o = align256(o + units * sizeof(int32_t));
+  w.part_ml = o;  o = align256(o + units * w.plan.wg_per_unit * G * 2 * sizeof(float));
+  w.part_o = o;   o = align256(o + units * w.plan.wg_per_unit * G * d->head_dim * sizeof(float));
+  w.total = o;
+  return w;
+}
+
+struct DenseWs {
+  size_t counters, part_ml, part_o, total;
+  int max_items;
+  fsa::AttnPlan plan;
+};
+
+DenseWs dense_ws(const fsa_dims* d, int32_t max_seq_len) {
+  DenseWs w;
+  const size_t units = (size_t)d->batch * d->num_kv_heads;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  w.max_items = n_pages_max(max_seq_len);
+  w.plan = fsa::plan_attention((int)units, w.max_items);
+  size_t o = 0;
+  w.counters = o; o = align256(o + units * sizeof(int32_t));
+  w.part_ml = o;  o = align256(o + units * w.plan.wg_per_unit * G * 2 * sizeof(float));
+  w.part_o = o;   o = align256(o + units * w.plan.wg_per_unit * G * d->head_dim * sizeof(float));
+  w.total = o;
+  return w;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fsa_last_error(void) { return g_err.c_str(); }
+
+fsa_status fsa_import_kv_plain(const fsa_dims* dims, const void* k_plain, const void* v_plain,
+                               void* k_cache, void* v_cache, void* stream) {
+  FSA_CHECK(check_dims(dims));
+  FSA_CHECK(need(k_plain, "k_plain"));
+  FSA_CHECK(need(v_plain, "v_plain"));
+  FSA_CHECK(need(k_cache, "k_cache"));
+  FSA_CHECK(need(v_cache, "v_cache"));
+  return hip_status(fsa::launch_import_kv_plain(
+                        static_cast<const uint16_t*>(k_plain), static_cast<const uint16_t*>(v_plain),
+                        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                        dims->num_pool_pages, dims->num_kv_heads, dims->head_dim,
+                        static_cast<hipStream_t>(stream)),
+                    "import_kv_plain launch");
+}
+
+fsa_status fsa_append_kv(const fsa_dims* dims, int32_t n_new, const void* k_new, const void* v_new,
+                         const int32_t* page_table, const int32_t* seq_lens, int32_t* seq_lens_out,
+                         void* k_cache, void* v_cache, void* meta, void* stream) {
+  FSA_CHECK(check_dims(dims));
+  if (n_new < 1) return fail(FSA_ERR_INVALID_ARG, "n_new must be >= 1");
+  FSA_CHECK(need(k_new, "k_new"));
+  FSA_CHECK(need(v_new, "v_new"));
+  FSA_CHECK(need(page_table, "page_table"));
+  FSA_CHECK(need(seq_lens, "seq_lens"));
+  FSA_CHECK(need(k_cache, "k_cache"));
+  FSA_CHECK(need(v_cache, "v_cache"));
+  FSA_CHECK(need(meta, "meta"));
+  if (seq_lens_out == seq_lens)
+    return fail(FSA_ERR_INVALID_ARG, "seq_lens_out must not alias seq_lens");
+  return hip_status(
+      fsa::launch_append_kv(n_new, static_cast<const uint16_t*>(k_new),
+                            static_cast<const uint16_t*>(v_new), page_table, seq_lens, seq_lens_out,
+                            static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                            static_cast<uint16_t*>(meta), dims->batch, dims->num_kv_heads,
+                            dims->head_dim, dims->max_pages_per_seq, static_cast<hipStream_t>(stream)),
+      "append_kv launch");
+}
+
+fsa_status fsa_build_page_meta(const fsa_dims* dims, const void* k_cache, const int32_t* page_table,
+                               const int32_t* seq_lens, void* meta, void* stream) {
+  FSA_CHECK(check_dims(dims));
+  FSA_CHECK(need(k_cache, "k_cache"));
+  FSA_CHECK(need(page_table, "page_table"));
+  FSA_CHECK(need(seq_lens, "seq_lens"));
+  FSA_CHECK(need(meta, "meta"));
+  return hip_status(
+      fsa::launch_build_page_meta(static_cast<const uint16_t*>(k_cache), page_table, seq_lens,
+                                  static_cast<uint16_t*>(meta), dims->batch, dims->num_kv_heads,
+                                  dims->head_dim, dims->max_pages_per_seq,
+                                  dims->max_pages_per_seq * dims->page_size,
+                                  static_cast<hipStream_t>(stream)),
+      "build_page_meta launch");
+}
+
+fsa_status fsa_quest_scores(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len,
+                            const void* q, const void* meta, const int32_t* page_table,
+                            const int32_t* seq_lens, float* scores, void* stream) {
+  FSA_CHECK(check_dims(dims));
+  FSA_CHECK(check_cfg(cfg));
+  FSA_CHECK(check_len(dims, max_seq_len));
+  FSA_CHECK(need(q, "q"));
+  FSA_CHECK(need(meta, "meta"));
+  FSA_CHECK(need(page_table, "page_table"));
+  FSA_CHECK(need(seq_lens, "seq_lens"));
+  FSA_CHECK(need(scores, "scores"));
+  return hip_status(
+      fsa::launch_quest_scores(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(meta),
+                               page_table, seq_lens, scores, dims->batch, dims->num_q_heads,
+                               dims->num_kv_heads, dims->head_dim, dims->max_pages_per_seq,
+                               cfg.prefix_tokens, cfg.window_tokens, max_seq_len,
+                               static_cast<hipStream_t>(stream)),
+      "quest_scores launch");
+}
+
+int32_t fsa_max_work_items(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len) {
+  if (check_dims(dims) != FSA_OK || check_cfg(cfg) != FSA_OK || check_len(dims, max_seq_len) != FSA_OK)
+    return -1;
+  return max_items_of(dims, cfg, max_seq_len);
+}
+
+fsa_status fsa_select_pages(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len,
+                            const float* scores, const int32_t* page_table, const int32_t* seq_lens,
+                            int32_t* sel_pages, int32_t* work, int32_t* counts, void* stream) {
+  FSA_CHECK(check_dims(dims));
+  FSA_CHECK(check_cfg(cfg));
+  FSA_CHECK(check_len(dims, max_seq_len));
+  FSA_CHECK(need(scores, "scores"));
+  FSA_CHECK(need(page_table, "page_table"));
+  FSA_CHECK(need(seq_lens, "seq_lens"));
+  return hip_status(fsa::launch_select_pages(scores, page_table, seq_lens, sel_pages, work, counts,
+                                             nullptr, dims->batch, dims->num_kv_heads,
+                                             dims->max_pages_per_seq, cfg.prefix_tokens,
+                                             cfg.window_tokens, cfg.budget_pages,
+                                             max_items_of(dims, cfg, max_seq_len), max_seq_len,
+                                             static_cast<hipStream_t>(stream)),
+                    "select_pages launch");
+}
+
+size_t fsa_sparse_decode_workspace_bytes(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len) {
+  if (check_dims(dims) != FSA_OK || check_cfg(cfg) != FSA_OK || check_len(dims, max_seq_len) != FSA_OK)
+    return 0;
+  return sparse_ws(dims, cfg, max_seq_len).total;
+}
+
+fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_scale,
+                                  int32_t max_seq_len, const void* q, const void* k_cache,
+                                  const void* v_cache, const void* meta, const int32_t* page_table,
+                                  const int32_t* seq_lens, void* out, int32_t* sel_pages,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  FSA_CHECK(check_dims(dims));
+  FSA_CHECK(check_cfg(cfg));
+  FSA_CHECK(check_len(dims, max_seq_len));
+  FSA_CHECK(need(q, "q"));
+  FSA_CHECK(need(k_cache, "k_cache"));
+  FSA_CHECK(need(v_cache, "v_cache"));
+  FSA_CHECK(need(meta, "meta"));
+  FSA_CHECK(need(page_table, "page_table"));
+  FSA_CHECK(need(seq_lens, "seq_lens"));
+  FSA_CHECK(need(out, "out"));
+  if (!(sm_scale > 0.f)) return fail(FSA_ERR_INVALID_ARG, "sm_scale must be > 0");
+  const SparseWs w = sparse_ws(dims, cfg, max_seq_len);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(FSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, w.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  FSA_CHECK(hip_status(
+      fsa::launch_quest_scores(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(meta),
+                               page_table, seq_lens, at<float>(workspace, w.scores), dims->batch,
+                               dims->num_q_heads, dims->num_kv_heads, dims->head_dim,
+                               dims->max_pages_per_seq, cfg.prefix_tokens, cfg.window_tokens,
+                               max_seq_len, st),
+      "quest_scores launch"));
+  FSA_CHECK(hip_status(
+      fsa::launch_select_pages(at<float>(workspace, w.scores), page_table, seq_lens, sel_pages,
+                               at<int32_t>(workspace, w.work), at<int32_t>(workspace, w.counts),
+                               at<int32_t>(workspace, w.counters), dims->batch, dims->num_kv_heads,
+                               dims->max_pages_per_seq, cfg.prefix_tokens, cfg.window_tokens,
+                               cfg.budget_pages, w.max_items, max_seq_len, st),
+      "select_pages launch"));
+  return hip_status(
+      fsa::launch_decode_attention(false, w.plan, static_cast<const uint16_t*>(q),
+                                   static_cast<const uint16_t*>(k_cache),
+                                   static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
+                                   at<int32_t>(workspace, w.work), at<int32_t>(workspace, w.counts),
+                                   at<float>(workspace, w.part_o), at<float>(workspace, w.part_ml),
+                                   at<int32_t>(workspace, w.counters), static_cast<uint16_t*>(out),
+                                   dims->batch, dims->num_q_heads, dims->num_kv_heads,
+                                   dims->head_dim, dims->max_pages_per_seq, w.max_items, sm_scale, max_seq_len,
+                                   st),
+      "decode_attention launch");
+}
+
+size_t fsa_dense_decode_workspace_bytes(const fsa_dims* dims, int32_t max_seq_len) {
+  if (check_dims(dims) != FSA_OK || check_len(dims, max_seq_len) != FSA_OK) return 0;
+  return dense_ws(dims, max_seq_len).total;
+}
+
+fsa_status fsa_dense_decode_attn(const fsa_dims* dims, float sm_scale, int32_t max_seq_len,
+                                 const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* page_table, const int32_t* seq_lens, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  FSA_CHECK(check_dims(dims));
+  FSA_CHECK(check_len(dims, max_seq_len));
+  FSA_CHECK(need(q, "q"));
+  FSA_CHECK(need(k_cache, "k_cache"));
+  FSA_CHECK(need(v_cache, "v_cache"));
+  FSA_CHECK(need(page_table, "page_table"));
+  FSA_CHECK(need(seq_lens, "seq_lens"));
+  FSA_CHECK(need(out, "out"));
+  if (!(sm_scale > 0.f)) return fail(FSA_ERR_INVALID_ARG, "sm_scale must be > 0");
+  const DenseWs w = dense_ws(dims, max_seq_len);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(FSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, w.total);
+  return hip_status(
+      fsa::launch_decode_attention(true, w.plan, static_cast<const uint16_t*>(q),
+                                   static_cast<const uint16_t*>(k_cache),
+                                   static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
+                                   nullptr, nullptr, at<float>(workspace, w.part_o),
+                                   at<float>(workspace, w.part_ml),
+                                   at<int32_t>(workspace, w.counters), static_cast<uint16_t*>(out),
+                                   dims->batch, dims->num_q_heads, dims->num_kv_heads,
+                                   dims->head_dim, dims->max_pages_per_seq, w.max_items, sm_scale,
+                                   max_seq_len, static_cast<hipStream_t>(stream)),
+      "dense decode_attention launch");
+}
+
+}  // extern "C"

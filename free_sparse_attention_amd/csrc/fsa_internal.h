@@ -1,0 +1,98 @@
+// Internal definitions shared by the gfx950 kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fsa {
+
+constexpr int kPage = 16;  // tokens per page
+constexpr int kWave = 64;  // CDNA wavefront width
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+// ---------------------------------------------------------------- bf16 bits
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// nearest-even fp32 -> bf16 bits (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Order-preserving map of bf16 bits to uint16 (numeric order, -0 just below +0).
+__device__ __forceinline__ uint32_t bf16_order_key(uint32_t b) {
+  return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+}
+// Inverse of bf16_order_key, with -0 written as +0.
+__device__ __forceinline__ uint32_t bf16_from_order_key(uint32_t k) {
+  uint32_t b = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+  return b == 0x8000u ? 0u : b;
+}
+
+// Order-preserving map of fp32 scores to uint32 (-0 and +0 map to one key).
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Streaming (non-temporal) loads of data read once per step.
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_nt(const uint2* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+
+// ---------------------------------------------------------------- launchers
+// All launchers enqueue on `stream` and return the launch status.
+
+hipError_t launch_import_kv_plain(const uint16_t* k_plain, const uint16_t* v_plain, uint16_t* kc,
+                                  uint16_t* vc, int pool, int hkv, int d, hipStream_t stream);
+
+hipError_t launch_append_kv(int n_new, const uint16_t* k_new, const uint16_t* v_new,
+                            const int32_t* page_table, const int32_t* seq_lens,
+                            int32_t* seq_lens_out, uint16_t* kc, uint16_t* vc, uint16_t* meta,
+                            int batch, int hkv, int d, int max_pages, hipStream_t stream);
+
+hipError_t launch_build_page_meta(const uint16_t* kc, const int32_t* page_table,
+                                  const int32_t* seq_lens, uint16_t* meta, int batch, int hkv,
+                                  int d, int max_pages, int max_seq_len, hipStream_t stream);
+
+hipError_t launch_quest_scores(const uint16_t* q, const uint16_t* meta, const int32_t* page_table,
+                               const int32_t* seq_lens, float* scores, int batch, int hq, int hkv,
+                               int d, int max_pages, int prefix, int window, int max_seq_len,
+                               hipStream_t stream);
+
+hipError_t launch_select_pages(const float* scores, const int32_t* page_table,
+                               const int32_t* seq_lens, int32_t* sel_pages, int32_t* work,
+                               int32_t* counts, int32_t* attn_counters, int batch, int hkv,
+                               int max_pages, int prefix, int window, int budget, int max_items,
+                               int max_seq_len, hipStream_t stream);
+
+struct AttnPlan {
+  int items_per_wave;  // work items each wave walks through
+  int wg_per_unit;     // workgroups launched per (b, KV head)
+};
+
+AttnPlan plan_attention(int units, int max_items);
+
+hipError_t launch_decode_attention(bool dense, const AttnPlan& plan, const uint16_t* q,
+                                   const uint16_t* kc, const uint16_t* vc,
+                                   const int32_t* page_table, const int32_t* seq_lens,
+                                   const int32_t* work, const int32_t* counts, float* part_o,
+                                   float* part_ml, int32_t* counters, uint16_t* out, int batch,
+                                   int hq, int hkv, int d, int max_pages, int max_items,
+                                   float sm_scale, int max_seq_len, hipStream_t stream);
+
+}  // namespace fsa

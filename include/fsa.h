@@ -1,0 +1,175 @@
+/*
+ * fsa.h -- combined sparse decode attention on gfx950 (AMD Instinct MI355X).
+ *
+ * One decode step of one full-attention layer: every query attends to the
+ * union of a pinned prefix, a sliding window of recent tokens and a fixed
+ * budget of KV pages picked query-aware from per-page key bounds.
+ *   - Paper "Accelerating Long-Context Decoding in Large-Scale Hybrid LLMs
+ *     Without Retraining" (Batista, Vatai, Wahib), Abstract: window, prefix and
+ *     a fixed budget of the most relevant tokens, configured per layer.
+ *   - Same paper, analysis page "Methodology" and digest page "The Move":
+ *     the budget is a Quest-style, query-aware paged top-k.
+ *   - Digest page "Why It Matters": the KV cache is kept at full size, so any
+ *     page can be selected.
+ *   - Quest (Tang et al., ICML 2024): per page the elementwise min m and max M
+ *     of its keys; sum_i max(q_i m_i, q_i M_i) bounds q.k over the page.
+ *
+ * Conventions for every entry point
+ *   - Pointers marked "device" point to GPU memory; the caller allocates and
+ *     owns every buffer (the library allocates nothing and keeps no state
+ *     besides a thread-local error message).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *     returns without synchronising.  Nothing is captured-unsafe: no
+ *     allocation, no memset, no host synchronisation.
+ *   - Host-detectable argument errors return a non-zero fsa_status before any
+ *     launch; fsa_last_error() then describes it.  A failed launch returns
+ *     FSA_ERR_HIP.  Device-resident data (page tables, lengths) is trusted.
+ *   - bf16 tensors are raw IEEE bfloat16 bit patterns.
+ *
+ * Device layouts (row-major, no padding)
+ *   q, out      bf16  [B][Hq][D]            query head h reads KV head h / (Hq/Hkv)
+ *   k_cache     bf16  [pool][Hkv][D/8][S][8] K of token slot j, channel c of a page
+ *                                           sits at [c/8][j][c%8]
+ *   v_cache     bf16  [pool][Hkv][D][S]      V stored channel-major inside a page
+ *   meta        bf16  [pool][Hkv][2][D]      [0] = elementwise min, [1] = max of the
+ *                                           page's valid keys; a zero is stored as +0
+ *   page_table  int32 [B][max_pages_per_seq] logical page -> pool page
+ *   seq_lens    int32 [B]                    tokens in the cache, including the
+ *                                           current token (the query's position
+ *                                           is seq_lens[b] - 1)
+ * Supported: D in {64, 128}; S = 16; Hq / Hkv in 1..16; seq_lens[b] >= 1.
+ */
+#ifndef FSA_H
+#define FSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FSA_OK = 0,
+  FSA_ERR_INVALID_ARG = 1, /* a null pointer, a negative size, an inconsistent shape */
+  FSA_ERR_UNSUPPORTED = 2, /* a shape outside the supported set above */
+  FSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the sizing call says */
+  FSA_ERR_HIP = 4          /* a HIP runtime call or launch failed */
+} fsa_status;
+
+typedef struct {
+  int32_t batch;             /* B */
+  int32_t num_q_heads;       /* Hq, a multiple of Hkv */
+  int32_t num_kv_heads;      /* Hkv */
+  int32_t head_dim;          /* D */
+  int32_t page_size;         /* S, tokens per page */
+  int32_t max_pages_per_seq; /* columns of page_table */
+  int32_t num_pool_pages;    /* pages in k_cache, v_cache and meta */
+} fsa_dims;
+
+/* Per-layer configuration (paper, Abstract: window and budget are chosen per
+ * layer; the prefix is pinned).  The attended set of a sequence of length L is
+ * [0, min(P, L)) U [max(0, L - W), L) U the tokens of the selected pages.
+ * Candidates for selection are the pages that intersect [min(P, L), L - W);
+ * k = min(budget_pages, candidates) of them are kept. */
+typedef struct {
+  int32_t prefix_tokens; /* P >= 0 */
+  int32_t window_tokens; /* W >= 0 */
+  int32_t budget_pages;  /* >= 0; P = W = budget = 0 is rejected */
+} fsa_layer_cfg;
+
+/* Text of the last non-OK status returned on the calling thread. */
+const char* fsa_last_error(void);
+
+/* Adopt a cache written in the common token-major paged layout: converts
+ * k_plain and v_plain, bf16 [pool][Hkv][S][D] (device), into k_cache and
+ * v_cache (device, layouts above) for every pool page.  Inputs and outputs
+ * must not overlap.  Metadata is not touched (see fsa_build_page_meta). */
+fsa_status fsa_import_kv_plain(const fsa_dims* dims, const void* k_plain, const void* v_plain,
+                               void* k_cache, void* v_cache, void* stream);
+
+/* Append n_new >= 1 tokens to every sequence and keep the page metadata
+ * current (Quest's per-page key min/max).  Token i of sequence b goes to
+ * position seq_lens[b] + i, i.e. page page_table[b][pos / S], slot pos % S;
+ * those page-table entries must already be mapped.
+ *   k_new, v_new  bf16 [B][n_new][Hkv][D] (device)
+ *   seq_lens      int32 [B] (device), lengths before the append
+ *   seq_lens_out  int32 [B] (device) or NULL; receives seq_lens[b] + n_new
+ *                 (may alias seq_lens)
+ * A page whose slot 0 is written by this call gets fresh metadata from the
+ * new tokens only; otherwise the new tokens' min/max are merged into the
+ * existing entry.  The result equals fsa_build_page_meta bit for bit. */
+fsa_status fsa_append_kv(const fsa_dims* dims, int32_t n_new, const void* k_new, const void* v_new,
+                         const int32_t* page_table, const int32_t* seq_lens, int32_t* seq_lens_out,
+                         void* k_cache, void* v_cache, void* meta, void* stream);
+
+/* Recompute the metadata of every page in use (logical pages
+ * [0, ceil(seq_lens[b] / S)) of every sequence) from k_cache, over each
+ * page's valid slots only.  Pool pages not in use are not written. */
+fsa_status fsa_build_page_meta(const fsa_dims* dims, const void* k_cache, const int32_t* page_table,
+                               const int32_t* seq_lens, void* meta, void* stream);
+
+/* Quest scores of the candidate pages.  For every (b, KV head g) and every
+ * candidate logical page p:
+ *     scores[b][g][p] = max over query heads h of group g of
+ *                       sum_i max(q[b][h][i] * m[p][i], q[b][h][i] * M[p][i])
+ * in fp32 (the group shares one selection; the maximum bounds every head).
+ * scores: fp32 [B][Hkv][max_pages_per_seq] (device); entries of
+ * non-candidate pages are not written.  max_seq_len is a host-side upper
+ * bound of seq_lens used to size the grid. */
+fsa_status fsa_quest_scores(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len,
+                            const void* q, const void* meta, const int32_t* page_table,
+                            const int32_t* seq_lens, float* scores, void* stream);
+
+/* Number of work items per (b, KV head) that fsa_select_pages can emit. */
+int32_t fsa_max_work_items(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len);
+
+/* Top-k selection and merge with the prefix and the window.
+ * For every (b, g): the k = min(budget, C) candidate pages with the largest
+ * scores; equal scores go to the lower logical page id; -0 equals +0.
+ *   sel_pages  int32 [B][Hkv][budget_pages] (device) or NULL: selected logical
+ *              page ids, ascending, then -1 padding
+ *   work       int32 [B][Hkv][max_items][4] (device) or NULL, max_items =
+ *              fsa_max_work_items(): the attended tokens as (logical page,
+ *              pool page, first slot, end slot) items in ascending token
+ *              order; every attended token appears in exactly one item
+ *   counts     int32 [B][Hkv][2] (device) or NULL: (k, number of items) */
+fsa_status fsa_select_pages(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len,
+                            const float* scores, const int32_t* page_table, const int32_t* seq_lens,
+                            int32_t* sel_pages, int32_t* work, int32_t* counts, void* stream);
+
+/* Workspace (device bytes) that fsa_sparse_decode_attn needs. */
+size_t fsa_sparse_decode_workspace_bytes(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len);
+
+/* The whole decode step: scores, selection and merge, then split-K flash
+ * decoding over the attended tokens (fp32 logits, online softmax and fp32
+ * accumulation) and the cross-split combine.
+ *   out        bf16 [B][Hq][D] (device): softmax(sm_scale * q.K) V over the
+ *              attended set, rounded to nearest-even bf16
+ *   sel_pages  as in fsa_select_pages, or NULL
+ *   workspace  device, at least fsa_sparse_decode_workspace_bytes(); no
+ *              initial contents needed; calls that share one workspace must
+ *              be ordered (same stream) */
+fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_scale,
+                                  int32_t max_seq_len, const void* q, const void* k_cache,
+                                  const void* v_cache, const void* meta, const int32_t* page_table,
+                                  const int32_t* seq_lens, void* out, int32_t* sel_pages,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace (device bytes) that fsa_dense_decode_attn needs. */
+size_t fsa_dense_decode_workspace_bytes(const fsa_dims* dims, int32_t max_seq_len);
+
+/* Plain decode attention over all tokens [0, seq_lens[b]) with the same
+ * split-K kernel: the baseline that the sparse step is measured against.
+ * The workspace must be zero-filled before its first use; every call leaves
+ * it ready for the next one. */
+fsa_status fsa_dense_decode_attn(const fsa_dims* dims, float sm_scale, int32_t max_seq_len,
+                                 const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* page_table, const int32_t* seq_lens, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSA_H */

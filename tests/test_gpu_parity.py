@@ -1,0 +1,268 @@
+"""GPU parity: every step of the HIP path against the CPU oracle.
+
+Acceptance, per step:
+  * page metadata: bit-exact;
+  * Quest scores: |gpu - oracle| <= 2e-5 |oracle| + 1e-6 (fp32 sums of 2D exact products);
+  * selection: identical sets wherever the oracle's k-th/(k+1)-th margin exceeds
+    1e-4 relative; otherwise |set| = k, it holds every page scoring above
+    s_k (1 + 1e-4) and nothing scoring below s_k (1 - 1e-4);
+  * work list: exactly the oracle's attended token set for the GPU's own
+    selection, each token once, ascending;
+  * output: |gpu - oracle| <= 2e-3 + 1e-2 |oracle| with the oracle run on the
+    GPU's selected pages (bf16 in, fp32 accumulate, bf16 out).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_harness import DeviceWorkload, bf16_f64, bits, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+S = 16
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import free_sparse_attention_amd as fsa
+    fsa.load()
+
+
+# ------------------------------------------------------------------ checks
+
+def meta_bits_oracle(K, L):
+    m, M = oracle.page_minmax(K, S)
+    f = lambda x: (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)  # exact: values are bf16
+    return f(m), f(M)
+
+
+def check_meta(dw, units=None):
+    wl = dw.wl
+    meta = bits(dw.meta)  # [pool][hkv][2][D]
+    units = units or [(b, g) for b in range(wl.batch) for g in range(wl.hkv)]
+    for b, g in units:
+        L = int(wl.seq_lens[b])
+        K = oracle.gather_keys(wl.k_pool, wl.page_table, b, g, L)
+        mo, Mo = meta_bits_oracle(K, L)
+        phys = wl.page_table[b, :mo.shape[0]]
+        assert np.array_equal(meta[phys, g, 0], mo), f"meta min differs, unit {(b, g)}"
+        assert np.array_equal(meta[phys, g, 1], Mo), f"meta max differs, unit {(b, g)}"
+
+
+def check_selection(sel_gpu, ora, budget):
+    cand = ora["candidates"]
+    s = ora["scores"]
+    k = min(budget, len(cand))
+    got = [int(p) for p in sel_gpu if p >= 0]
+    assert len(got) == k and all(p == -1 for p in sel_gpu[k:])
+    assert got == sorted(got)
+    if ora["margin"] > 1e-4:
+        assert got == ora["selected"].tolist()
+    else:
+        sk = np.sort(s)[::-1][k - 1]
+        by_page = dict(zip(cand.tolist(), s.tolist()))
+        must = {p for p, v in by_page.items() if v > sk + 1e-4 * abs(sk)}
+        may = {p for p, v in by_page.items() if v >= sk - 1e-4 * abs(sk)}
+        assert must <= set(got) <= may
+
+
+def check_out(gpu, ref, what=""):
+    err = np.abs(gpu - ref)
+    tol = 2e-3 + 1e-2 * np.abs(ref)
+    bad = err > tol
+    assert not bad.any(), f"{what}: {bad.sum()} outputs off, max err {err.max():.3e}"
+
+
+def items_to_tokens(items, n, L, page_row):
+    toks = []
+    for p, phys, lo, hi in items[:n]:
+        assert 0 <= lo < hi <= S, (p, lo, hi)
+        assert phys == page_row[p]
+        toks.extend(range(p * S + lo, p * S + hi))
+    assert toks == sorted(toks) and len(set(toks)) == len(toks)
+    mask = np.zeros(L, bool)
+    mask[toks] = True
+    return mask
+
+
+def run_and_check(wl, cfg=None, units=None, q=None, check_scores=True, dense=True, max_seq_len=None,
+                  dw=None):
+    """Full step on the GPU; compare every stage with the oracle on `units`."""
+    cfg = tuple(cfg if cfg is not None else wl.cfg)
+    say(f"[case] {wl.name} B={wl.batch} Hq={wl.hq} Hkv={wl.hkv} D={wl.d} L={wl.seq_lens.tolist()[:4]} "
+        f"cfg={cfg} permuted={wl.permuted}")
+    dw = dw or DeviceWorkload(wl)
+    units = units or [(b, g) for b in range(wl.batch) for g in range(wl.hkv)]
+    qd = dw.q if q is None else to_dev_bf16(q)
+    qbits = wl.q if q is None else q
+    check_meta(dw, units)
+    scores = dw.scores(cfg, q=qd, max_seq_len=max_seq_len).cpu().numpy()
+    sel_s, work, counts = dw.select(torch.from_numpy(scores).cuda(), cfg, max_seq_len=max_seq_len)
+    out, sel = dw.sparse(cfg, q=qd, max_seq_len=max_seq_len)
+    torch.cuda.synchronize()
+    out = bf16_f64(out)
+    sel = sel.cpu().numpy() if sel is not None else None
+    sel_s = sel_s.cpu().numpy()
+    work = work.cpu().numpy()
+    counts = counts.cpu().numpy()
+    dout = bf16_f64(dw.dense(q=qd, max_seq_len=max_seq_len)) if dense else None
+    G = wl.group
+    for b, g in units:
+        L = int(wl.seq_lens[b])
+        qf, K, V = oracle.unit_inputs(wl, b, g, q_bits=qbits)
+        ora = oracle.sparse_decode_unit(qf, K, V, L, cfg, S, wl.sm_scale)
+        cand = ora["candidates"]
+        if check_scores and len(cand):
+            gs = scores[b, g, cand]
+            assert np.all(np.abs(gs - ora["scores"]) <= 2e-5 * np.abs(ora["scores"]) + 1e-6), f"scores {(b, g)}"
+        if cfg[2] > 0:
+            check_selection(sel[b, g], ora, cfg[2])
+            assert np.array_equal(sel[b, g], sel_s[b, g]), "composite and stand-alone selection differ"
+        k_gpu = int(counts[b, g, 0])
+        assert k_gpu == min(cfg[2], len(cand))
+        gsel = [int(p) for p in sel[b, g][:k_gpu]] if cfg[2] > 0 else []
+        mask_gpu = items_to_tokens(work[b, g], int(counts[b, g, 1]), L, wl.page_table[b])
+        mask_ora = oracle.attended_mask(L, cfg[0], cfg[1], S, gsel)
+        assert np.array_equal(mask_gpu, mask_ora), f"attended set {(b, g)}"
+        ref = oracle.attend(qf, K, V, mask_ora, wl.sm_scale)
+        check_out(out[b, g * G:(g + 1) * G], ref, f"sparse out {(b, g)}")
+        if dense:
+            check_out(dout[b, g * G:(g + 1) * G], oracle.dense_decode_unit(qf, K, V, wl.sm_scale),
+                      f"dense out {(b, g)}")
+    return dw, out, sel
+
+
+# ------------------------------------------------------------------ small cases
+
+def test_tiny_end_to_end():
+    wl = synth.make_workload("tiny")
+    dw, out, sel = run_and_check(wl)
+    for g in range(wl.hkv):  # every needle page is picked (any page can be selected)
+        assert set((wl.needles[0] // S).tolist()) <= set(sel[0, g].tolist())
+
+
+@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 8), (64, 4, 2), (128, 16, 4), (128, 32, 4), (128, 16, 1), (64, 12, 4)])
+def test_shapes(d, hq, hkv):
+    wl = synth.workloads.build(name=f"shape{d}_{hq}_{hkv}", seed=11, batch=3, hq=hq, hkv=hkv, d=d,
+                               seq_lens=(1500, 3001, 777), prefix=32, window=200, budget=9, k_sigma=0.5,
+                               n_needles=4, permuted=True)
+    run_and_check(wl)
+
+
+@pytest.mark.parametrize("cfg", [(0, 0, 5), (0, 300, 0), (100, 0, 0), (37, 53, 6), (64, 256, 10**5),
+                                 (5000, 16, 3), (16, 5000, 3), (0, 1, 1)])
+def test_configs_and_degenerate_regions(cfg):
+    wl = synth.workloads.build(name="cfgs", seed=12, batch=2, hq=8, hkv=2, d=64, seq_lens=(2049, 600),
+                               prefix=cfg[0], window=cfg[1], budget=cfg[2], k_sigma=0.3, permuted=True)
+    run_and_check(wl)
+
+
+@pytest.mark.parametrize("L", [1, 2, 15, 16, 17, 31, 33, 100])
+def test_short_sequences(L):
+    wl = synth.workloads.build(name="short", seed=13, batch=2, hq=4, hkv=1, d=128, seq_lens=(L, L + 5),
+                               prefix=4, window=8, budget=1, permuted=False)
+    run_and_check(wl)
+
+
+def test_all_scores_tie_takes_lowest_ids():
+    wl = synth.workloads.build(name="ties", seed=14, batch=1, hq=8, hkv=2, d=64, seq_lens=(3000,),
+                               prefix=64, window=256, budget=20)
+    wl.k_pool[:] = 0
+    dw, out, sel = run_and_check(wl)
+    first = oracle.candidate_pages(3000, 64, 256, S)[:20].tolist()
+    for g in range(2):
+        assert sel[0, g].tolist() == first
+
+
+def test_full_budget_equals_dense():
+    wl = synth.workloads.build(name="fullbudget", seed=15, batch=2, hq=16, hkv=4, d=128, seq_lens=(5000, 4111),
+                               prefix=64, window=512, budget=10**6, k_sigma=0.5, permuted=True)
+    dw, out, sel = run_and_check(wl)
+    dense = bf16_f64(dw.dense())
+    check_out(out, dense, "sparse(full budget) vs dense")
+
+
+def test_repeat_is_bitwise_deterministic_and_plan_invariant():
+    wl = synth.workloads.build(name="determinism", seed=16, batch=2, hq=16, hkv=4, d=128, seq_lens=(20000, 9000),
+                               prefix=128, window=1024, budget=64, k_sigma=0.5, n_needles=8, permuted=True)
+    dw = DeviceWorkload(wl)
+    ws = dw.workspace()
+    ref, rsel = dw.sparse(ws=ws)
+    ref = bits(ref)
+    rsel = rsel.cpu().numpy()
+    for _ in range(20):
+        o, s = dw.sparse(ws=ws)
+        assert np.array_equal(bits(o), ref) and np.array_equal(s.cpu().numpy(), rsel)
+    # a larger host bound changes the grid (split sizes); results agree to fp32 rounding
+    o2, s2 = dw.sparse(max_seq_len=wl.max_pages * S)
+    assert np.array_equal(s2.cpu().numpy(), rsel)
+    a, b_ = bf16_f64(o2), synth.bf16_bits_to_f64(ref)
+    assert np.all(np.abs(a - b_) <= 2 ** -7 * np.abs(b_) + 1e-5)
+
+
+# ------------------------------------------------------------------ append
+
+def test_append_matches_rebuild_and_oracle():
+    """Single-token and chunked appends keep the metadata equal (bit for bit) to a
+    rebuild and to the oracle; decoding after the appends matches the oracle."""
+    wl = synth.workloads.build(name="append", seed=17, batch=3, hq=8, hkv=2, d=128, seq_lens=(1000, 16, 2047),
+                               prefix=32, window=128, budget=8, k_sigma=0.5, permuted=True, extra_tokens=200)
+    import free_sparse_attention_amd as fsa
+    dw = DeviceWorkload(wl)
+    lens = torch.from_numpy(wl.seq_lens.copy()).cuda()
+    lens2 = torch.empty_like(lens)
+    chunks = [1, 1, 1, 37, 1, 16, 100, 1]
+    for step, n in enumerate(chunks):
+        say(f"[append] step {step} n_new={n}")
+        kn, vn = _tokens_at(wl, lens.cpu().numpy(), n)
+        fsa.append_kv(dw.dims, n, to_dev_bf16(kn), to_dev_bf16(vn), dw.page_table, lens, lens2, dw.k_cache,
+                      dw.v_cache, dw.meta)
+        # keep the oracle's plain pool in step
+        L0 = lens.cpu().numpy()
+        for b in range(wl.batch):
+            for i in range(n):
+                t = int(L0[b]) + i
+                phys = wl.page_table[b, t // S]
+                wl.k_pool[phys, :, t % S, :] = kn[b, i]
+                wl.v_pool[phys, :, t % S, :] = vn[b, i]
+        lens, lens2 = lens2, lens
+        assert (lens.cpu().numpy() == L0 + n).all()
+        wl.seq_lens = lens.cpu().numpy().astype(np.int32)
+        rebuilt = torch.zeros_like(dw.meta)
+        dw.seq_lens = lens
+        fsa.build_page_meta(dw.dims, dw.k_cache, dw.page_table, lens, rebuilt)
+        torch.cuda.synchronize()
+        mb, rb = bits(dw.meta), bits(rebuilt)
+        for b in range(wl.batch):
+            used = wl.page_table[b, :-(-int(wl.seq_lens[b]) // S)]
+            assert np.array_equal(mb[used], rb[used]), f"append vs rebuild, seq {b}"
+    dw.max_seq_len = int(wl.seq_lens.max())
+    # the converted caches equal a fresh import of the oracle's plain pool
+    fresh = DeviceWorkload(wl)
+    for b in range(wl.batch):
+        used = wl.page_table[b, :-(-int(wl.seq_lens[b]) // S)]
+        assert np.array_equal(bits(fresh.k_cache)[used], bits(dw.k_cache)[used])
+        assert np.array_equal(bits(fresh.v_cache)[used], bits(dw.v_cache)[used])
+    run_and_check(wl, dw=dw)
+
+
+def _tokens_at(wl, lens, n):
+    kk, kv, _ = wl.keys()
+    kn = np.empty((wl.batch, n, wl.hkv, wl.d), np.uint16)
+    vn = np.empty_like(kn)
+    for b in range(wl.batch):
+        kn[b] = synth.core.fill_tokens(kk, b, int(lens[b]), n, wl.hkv, wl.d, wl.k_scale)
+        vn[b] = synth.core.fill_tokens(kv, b, int(lens[b]), n, wl.hkv, wl.d, None)
+    return kn, vn
