@@ -39,8 +39,7 @@ def alg_bytes(wl):
     """Algorithmic bytes of one step and of one quest-score launch.
 
     Per (sequence b, KV head g) unit with C candidate pages and T attended tokens:
-      score kernel: 4 D C (metadata min+max, bf16) + 4 C (fp32 score written)
-                    + 2 G D (q) ; page-table entries 4 C once per sequence
+      score kernel: 4 D C (metadata min+max, bf16) + 4 C (fp32 score written) + 2 G D (q)
       whole step:   metadata 4 D C + K/V 4 D T + q and out 4 G D + page table 4 n per sequence
     """
     S, D, G = wl.page, wl.d, wl.group
@@ -54,7 +53,7 @@ def alg_bytes(wl):
         # attended tokens: prefix + window + middle tokens of k pages (full pages in the bulk)
         T = Pe + (L - max(Ws, Pe)) + min(k * S, max(0, Ws - Pe))
         n = -(-L // S)
-        score += wl.hkv * (4 * D * C + 4 * C + 2 * G * D) + 4 * C
+        score += wl.hkv * (4 * D * C + 4 * C + 2 * G * D)
         step += wl.hkv * (4 * D * C + 4 * D * T + 4 * G * D) + 4 * n
     return score, step
 
@@ -138,7 +137,7 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
 
     def score(i):
         k, v, m = reps[i % R]
-        fsa.quest_scores(base.dims, c, msl, base.q, m, base.page_table, base.seq_lens, scores, stream)
+        fsa.quest_scores(base.dims, c, msl, base.q, m, base.seq_lens, scores, stream)
 
     n_k = reps_kernel or max(steps, 50)
     ms_score = timed(score, n_k, 10)

@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     import_kv_plain,
     load,
     max_work_items,
+    meta_bytes,
     quest_scores,
     select_pages,
     sparse_decode_attn,

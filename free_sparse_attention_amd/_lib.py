@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libfsa.so")
 FSA_OK, FSA_ERR_INVALID_ARG, FSA_ERR_UNSUPPORTED, FSA_ERR_WORKSPACE, FSA_ERR_HIP = range(5)
 
 EXPORTED = (
-    "fsa_last_error", "fsa_import_kv_plain", "fsa_append_kv", "fsa_build_page_meta",
+    "fsa_last_error", "fsa_import_kv_plain", "fsa_append_kv", "fsa_build_page_meta", "fsa_meta_bytes",
     "fsa_quest_scores", "fsa_max_work_items", "fsa_select_pages",
     "fsa_sparse_decode_workspace_bytes", "fsa_sparse_decode_attn",
     "fsa_dense_decode_workspace_bytes", "fsa_dense_decode_attn",
@@ -64,7 +64,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             "fsa_import_kv_plain": (i32, [D, vp, vp, vp, vp, vp]),
             "fsa_append_kv": (i32, [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "fsa_build_page_meta": (i32, [D, vp, vp, vp, vp, vp]),
-            "fsa_quest_scores": (i32, [D, C, i32, vp, vp, vp, vp, vp, vp]),
+            "fsa_meta_bytes": (sz, [D]),
+            "fsa_quest_scores": (i32, [D, C, i32, vp, vp, vp, vp, vp]),
             "fsa_max_work_items": (i32, [D, C, i32]),
             "fsa_select_pages": (i32, [D, C, i32, vp, vp, vp, vp, vp, vp, vp]),
             "fsa_sparse_decode_workspace_bytes": (sz, [D, C, i32]),
@@ -134,10 +135,16 @@ def build_page_meta(d: Dims, k_cache, page_table, seq_lens, meta, stream=None):
                                       _i32(seq_lens, "seq_lens"), _p(meta, "meta", 2), _stream(stream)))
 
 
-def quest_scores(d: Dims, c: LayerCfg, max_seq_len, q, meta, page_table, seq_lens, scores, stream=None):
+def meta_bytes(d: Dims) -> int:
+    n = load().fsa_meta_bytes(ctypes.byref(d))
+    if n == 0:
+        raise FsaError(FSA_ERR_INVALID_ARG, load().fsa_last_error().decode())
+    return n
+
+
+def quest_scores(d: Dims, c: LayerCfg, max_seq_len, q, meta, seq_lens, scores, stream=None):
     _check(load().fsa_quest_scores(ctypes.byref(d), c, int(max_seq_len), _p(q, "q", 2), _p(meta, "meta", 2),
-                                   _i32(page_table, "page_table"), _i32(seq_lens, "seq_lens"),
-                                   _p(scores, "scores", 4), _stream(stream)))
+                                   _i32(seq_lens, "seq_lens"), _p(scores, "scores", 4), _stream(stream)))
 
 
 def max_work_items(d: Dims, c: LayerCfg, max_seq_len) -> int:

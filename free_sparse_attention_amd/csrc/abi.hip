@@ -67,6 +67,9 @@ fsa_status check_len(const fsa_dims* d, int32_t max_seq_len) {
   if (max_seq_len < 1 || (long long)max_seq_len > (long long)d->max_pages_per_seq * d->page_size)
     return fail(FSA_ERR_INVALID_ARG, "max_seq_len %d outside [1, max_pages_per_seq * page_size]",
                 max_seq_len);
+  if ((max_seq_len + fsa::kPage - 1) / fsa::kPage > fsa::select_max_candidates())
+    return fail(FSA_ERR_UNSUPPORTED, "max_seq_len %d: more than %d pages per sequence", max_seq_len,
+                fsa::select_max_candidates());
   return FSA_OK;
 }
 
@@ -88,9 +91,9 @@ int max_items_of(const fsa_dims* d, fsa_layer_cfg c, int32_t max_seq_len) {
   return (int)std::max<long>(1, pre + sel + win);
 }
 
-// Workspace of the sparse step: [scores][work][counts][counters][part_ml][part_o]
+// Workspace of the sparse step: [scores][work][counts][part_ml][part_o]
 struct SparseWs {
-  size_t scores, work, counts, counters, part_ml, part_o, total;
+  size_t scores, work, counts, part_ml, part_o, total;
   int max_items;
   fsa::AttnPlan plan;
 };
@@ -105,7 +108,6 @@ SparseWs sparse_ws(const fsa_dims* d, fsa_layer_cfg c, int32_t max_seq_len) {
   w.scores = o;   o = align256(o + units * d->max_pages_per_seq * sizeof(float));
   w.work = o;     o = align256(o + units * w.max_items * 4 * sizeof(int32_t));
   w.counts = o;   o = align256(o + units * 2 * sizeof(int32_t));
-  w.counters = o; o = align256(o + units * sizeof(int32_t));
   w.part_ml = o;  o = align256(o + units * w.plan.wg_per_unit * G * 2 * sizeof(float));
   w.part_o = o;   o = align256(o + units * w.plan.wg_per_unit * G * d->head_dim * sizeof(float));
   w.total = o;
@@ -113,7 +115,7 @@ SparseWs sparse_ws(const fsa_dims* d, fsa_layer_cfg c, int32_t max_seq_len) {
 }
 
 struct DenseWs {
-  size_t counters, part_ml, part_o, total;
+  size_t part_ml, part_o, total;
   int max_items;
   fsa::AttnPlan plan;
 };
@@ -125,7 +127,6 @@ DenseWs dense_ws(const fsa_dims* d, int32_t max_seq_len) {
   w.max_items = n_pages_max(max_seq_len);
   w.plan = fsa::plan_attention((int)units, w.max_items);
   size_t o = 0;
-  w.counters = o; o = align256(o + units * sizeof(int32_t));
   w.part_ml = o;  o = align256(o + units * w.plan.wg_per_unit * G * 2 * sizeof(float));
   w.part_o = o;   o = align256(o + units * w.plan.wg_per_unit * G * d->head_dim * sizeof(float));
   w.total = o;
@@ -198,23 +199,27 @@ fsa_status fsa_build_page_meta(const fsa_dims* dims, const void* k_cache, const 
 }
 
 fsa_status fsa_quest_scores(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len,
-                            const void* q, const void* meta, const int32_t* page_table,
-                            const int32_t* seq_lens, float* scores, void* stream) {
+                            const void* q, const void* meta, const int32_t* seq_lens, float* scores,
+                            void* stream) {
   FSA_CHECK(check_dims(dims));
   FSA_CHECK(check_cfg(cfg));
   FSA_CHECK(check_len(dims, max_seq_len));
   FSA_CHECK(need(q, "q"));
   FSA_CHECK(need(meta, "meta"));
-  FSA_CHECK(need(page_table, "page_table"));
   FSA_CHECK(need(seq_lens, "seq_lens"));
   FSA_CHECK(need(scores, "scores"));
   return hip_status(
       fsa::launch_quest_scores(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(meta),
-                               page_table, seq_lens, scores, dims->batch, dims->num_q_heads,
-                               dims->num_kv_heads, dims->head_dim, dims->max_pages_per_seq,
-                               cfg.prefix_tokens, cfg.window_tokens, max_seq_len,
-                               static_cast<hipStream_t>(stream)),
+                               seq_lens, scores, dims->batch, dims->num_q_heads, dims->num_kv_heads,
+                               dims->head_dim, dims->max_pages_per_seq, cfg.prefix_tokens,
+                               cfg.window_tokens, max_seq_len, static_cast<hipStream_t>(stream)),
       "quest_scores launch");
+}
+
+size_t fsa_meta_bytes(const fsa_dims* dims) {
+  if (check_dims(dims) != FSA_OK) return 0;
+  return (size_t)dims->batch * dims->num_kv_heads * fsa::meta_tiles(dims->max_pages_per_seq) *
+         fsa::kMetaTile * 2 * dims->head_dim * sizeof(uint16_t);
 }
 
 int32_t fsa_max_work_items(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len) {
@@ -233,7 +238,7 @@ fsa_status fsa_select_pages(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max
   FSA_CHECK(need(page_table, "page_table"));
   FSA_CHECK(need(seq_lens, "seq_lens"));
   return hip_status(fsa::launch_select_pages(scores, page_table, seq_lens, sel_pages, work, counts,
-                                             nullptr, dims->batch, dims->num_kv_heads,
+                                             dims->batch, dims->num_kv_heads,
                                              dims->max_pages_per_seq, cfg.prefix_tokens,
                                              cfg.window_tokens, cfg.budget_pages,
                                              max_items_of(dims, cfg, max_seq_len), max_seq_len,
@@ -269,7 +274,7 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
   hipStream_t st = static_cast<hipStream_t>(stream);
   FSA_CHECK(hip_status(
       fsa::launch_quest_scores(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(meta),
-                               page_table, seq_lens, at<float>(workspace, w.scores), dims->batch,
+                               seq_lens, at<float>(workspace, w.scores), dims->batch,
                                dims->num_q_heads, dims->num_kv_heads, dims->head_dim,
                                dims->max_pages_per_seq, cfg.prefix_tokens, cfg.window_tokens,
                                max_seq_len, st),
@@ -277,7 +282,7 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
   FSA_CHECK(hip_status(
       fsa::launch_select_pages(at<float>(workspace, w.scores), page_table, seq_lens, sel_pages,
                                at<int32_t>(workspace, w.work), at<int32_t>(workspace, w.counts),
-                               at<int32_t>(workspace, w.counters), dims->batch, dims->num_kv_heads,
+                               dims->batch, dims->num_kv_heads,
                                dims->max_pages_per_seq, cfg.prefix_tokens, cfg.window_tokens,
                                cfg.budget_pages, w.max_items, max_seq_len, st),
       "select_pages launch"));
@@ -287,7 +292,7 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
                                    static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
                                    at<int32_t>(workspace, w.work), at<int32_t>(workspace, w.counts),
                                    at<float>(workspace, w.part_o), at<float>(workspace, w.part_ml),
-                                   at<int32_t>(workspace, w.counters), static_cast<uint16_t*>(out),
+                                   static_cast<uint16_t*>(out),
                                    dims->batch, dims->num_q_heads, dims->num_kv_heads,
                                    dims->head_dim, dims->max_pages_per_seq, w.max_items, sm_scale, max_seq_len,
                                    st),
@@ -320,8 +325,7 @@ fsa_status fsa_dense_decode_attn(const fsa_dims* dims, float sm_scale, int32_t m
                                    static_cast<const uint16_t*>(k_cache),
                                    static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
                                    nullptr, nullptr, at<float>(workspace, w.part_o),
-                                   at<float>(workspace, w.part_ml),
-                                   at<int32_t>(workspace, w.counters), static_cast<uint16_t*>(out),
+                                   at<float>(workspace, w.part_ml), static_cast<uint16_t*>(out),
                                    dims->batch, dims->num_q_heads, dims->num_kv_heads,
                                    dims->head_dim, dims->max_pages_per_seq, w.max_items, sm_scale,
                                    max_seq_len, static_cast<hipStream_t>(stream)),

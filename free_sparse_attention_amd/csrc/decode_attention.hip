@@ -1,5 +1,4 @@
-// Split-K flash decoding over the attended pages, with the cross-split
-// combine fused into the last workgroup of each (sequence, KV head).
+// Split-K flash decoding over the attended pages, then the cross-split combine.
 //
 // Per work item (one page, a token range [lo, hi) inside it), one wave:
 //   S^T[token][head] = K[token][:] . q[head][:]     v_mfma_f32_16x16x32_bf16, D/32 steps
@@ -10,33 +9,37 @@
 // is exactly the B-operand layout the PV product needs, so P never leaves
 // registers.  The cache layouts make every operand load a coalesced read
 // straight from HBM: a K page [D/8][16][8] is read as D/32 contiguous
-// 1 KiB rows, a V page [D][16] as D/16 contiguous 512-byte rows.
+// 1 KiB rows, a V page [D][16] as D/16 contiguous 512-byte rows.  Each wave
+// walks a run of items with the next page's loads in flight while the current
+// page is computed.
 //
-// Four waves per workgroup each walk their own run of items; the workgroup
-// merges its waves' (max, sum, accumulator) through LDS, writes one partial,
-// and the last workgroup of the unit to finish (agent-scope atomic ticket)
-// combines all partials:  o = sum_j 2^(m_j - m) o_j / sum_j 2^(m_j - m) l_j.
+// Four waves per workgroup; the workgroup merges its waves' (max, sum,
+// accumulator) through LDS and writes one partial (or the final output when
+// the unit has a single workgroup).  A second kernel combines partials:
+//   o = sum_j 2^(m_j - m) o_j / sum_j 2^(m_j - m) l_j,  m = max_j m_j.
 #include "fsa_internal.h"
 
 namespace fsa {
 namespace {
 
 constexpr int kAttnWaves = 4;
+constexpr int kMaxItemsPerWave = 64;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
+__device__ __forceinline__ int wave_bcast(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
 template <int D, bool DENSE>
-__global__ __launch_bounds__(256) void decode_attention_kernel(
+__global__ __launch_bounds__(256, 3) void decode_attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ work,
     const int32_t* __restrict__ counts, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int32_t* __restrict__ counters, uint16_t* __restrict__ out, int hq, int hkv, int max_pages,
-    int max_items, int ipw, int wg_per_unit, float scale_log2, int max_seq_len) {
+    uint16_t* __restrict__ out, int hq, int hkv, int max_pages, int max_items, int ipw,
+    int wg_per_unit, float scale_log2, int max_seq_len) {
   constexpr int NKS = D / 32;  // QK k-steps
   constexpr int NDT = D / 16;  // PV d-tiles
   __shared__ float sh_o[kAttnWaves][D][17];
   __shared__ float sh_m[kAttnWaves][16], sh_l[kAttnWaves][16];
-  __shared__ int sh_last;
 
   const int unit = blockIdx.x / wg_per_unit, wg = blockIdx.x % wg_per_unit;
   const int b = unit / hkv, g = unit % hkv, G = hq / hkv;
@@ -48,15 +51,31 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
   const int n_wg = (n_items + per_wg - 1) / per_wg;
   if (wg >= n_wg) return;
   const int i_begin = wg * per_wg + wave * ipw;
-  const int i_end = min(i_begin + ipw, n_items);
+  const int n = max(0, min(ipw, n_items - i_begin));
+
+  // item descriptors of this wave: lane j holds item i_begin + j
+  const int32_t* pt = page_table + (size_t)b * max_pages;
+  int my_phys = 0, my_lo = 0, my_hi = 0;
+  if (lane < n) {
+    const int i = i_begin + lane;
+    if (DENSE) {
+      my_phys = pt[i];
+      my_hi = min(kPage, L - i * kPage);
+    } else {
+      const int4 it = *reinterpret_cast<const int4*>(work + 4 * ((size_t)unit * max_items + i));
+      my_phys = it.y;
+      my_lo = it.z;
+      my_hi = it.w;
+    }
+  }
 
   // B operand of QK: q[head col][32 ks + 8 gq .. +8] (zero rows beyond G)
   bf16x8_t qb[NKS];
-  const uint16_t* qrow = q + ((size_t)b * hq + (size_t)g * G + col) * D;
+  const uint16_t* qrow = q + ((size_t)b * hq + (size_t)g * G + min(col, G - 1)) * D;
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    uint4 r = make_uint4(0, 0, 0, 0);
-    if (col < G) r = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * gq);
+    uint4 r = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * gq);
+    if (col >= G) r = make_uint4(0, 0, 0, 0);
     qb[ks] = __builtin_bit_cast(bf16x8_t, r);
   }
 
@@ -65,35 +84,23 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
 #pragma unroll
   for (int j = 0; j < NDT; ++j) acc[j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* pt = page_table + (size_t)b * max_pages;
-  const int32_t* wl = work + 4 * (size_t)unit * max_items;
-  for (int i = i_begin; i < i_end; ++i) {
-    int phys, lo, hi;
-    if (DENSE) {
-      phys = pt[i];
-      lo = 0;
-      hi = min(kPage, L - i * kPage);
-    } else {
-      const int4 it = *reinterpret_cast<const int4*>(wl + 4 * (size_t)i);
-      phys = it.y;
-      lo = it.z;
-      hi = it.w;
-    }
-    const size_t blk = ((size_t)phys * hkv + g) * (kPage * D);
-    uint4 kr[NKS];
-    uint2 vr[NDT];
+  const size_t head_off = (size_t)g * (kPage * D);
+  const size_t page_stride = (size_t)hkv * (kPage * D);
+  auto load = [&](int j, uint4 (&kr)[NKS], uint2 (&vr)[NDT]) {
+    const size_t blk = (size_t)wave_bcast(my_phys, j) * page_stride + head_off;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
       kr[ks] = ld_nt(reinterpret_cast<const uint4*>(kc + blk + (size_t)(64 * ks + lane) * 8));
 #pragma unroll
-    for (int j = 0; j < NDT; ++j)
-      vr[j] = ld_nt(reinterpret_cast<const uint2*>(vc + blk + (size_t)(16 * j + col) * kPage + 4 * gq));
-
+    for (int t = 0; t < NDT; ++t)
+      vr[t] = ld_nt(reinterpret_cast<const uint2*>(vc + blk + (size_t)(16 * t + col) * kPage + 4 * gq));
+  };
+  auto compute = [&](int j, const uint4 (&kr)[NKS], const uint2 (&vr)[NDT]) {
+    const int lo = wave_bcast(my_lo, j), hi = wave_bcast(my_hi, j);
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[ks]), qb[ks], s, 0, 0, 0);
-
     float x[4], mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -117,10 +124,33 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
     const uint32_t p23 = f32_to_bf16_bits(p[2]) | (f32_to_bf16_bits(p[3]) << 16);
     const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
 #pragma unroll
-    for (int j = 0; j < NDT; ++j) {
-      acc[j] *= alpha;
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, vr[j]), pb,
-                                                         acc[j], 0, 0, 0);
+    for (int t = 0; t < NDT; ++t) {
+      acc[t] *= alpha;
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, vr[t]), pb, acc[t], 0, 0, 0);
+    }
+  };
+
+  // Two-stage pipeline.  Every trip of the loop issues exactly one page of
+  // loads and consumes one, so the number of loads in flight at the loop head
+  // is the same on entry and on the back edge and the compiler waits only for
+  // the page about to be used; the last one or two pages are peeled.
+  uint4 kA[NKS], kB[NKS];
+  uint2 vA[NDT], vB[NDT];
+  if (n > 0) {
+    load(0, kA, vA);
+    int j = 0;
+    for (; j + 2 < n; j += 2) {
+      load(j + 1, kB, vB);
+      compute(j, kA, vA);
+      load(j + 2, kA, vA);
+      compute(j + 1, kB, vB);
+    }
+    if (j + 1 < n) {
+      load(j + 1, kB, vB);
+      compute(j, kA, vA);
+      compute(j + 1, kB, vB);
+    } else {
+      compute(j, kA, vA);
     }
   }
   l_run += __shfl_xor(l_run, 16);
@@ -132,16 +162,15 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
     sh_l[wave][col] = l_run;
   }
 #pragma unroll
-  for (int j = 0; j < NDT; ++j)
+  for (int t = 0; t < NDT; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sh_o[wave][16 * j + 4 * gq + r][col] = acc[j][r];
+    for (int r = 0; r < 4; ++r) sh_o[wave][16 * t + 4 * gq + r][col] = acc[t][r];
   __syncthreads();
 
-  const int nout = G * D;
   const bool single = (n_wg == 1);
   float* po = part_o + ((size_t)unit * wg_per_unit + wg) * G * D;
   float* pml = part_ml + 2 * ((size_t)unit * wg_per_unit + wg) * G;
-  for (int idx = threadIdx.x; idx < nout; idx += 256) {
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
     const int h = idx / D, d = idx % D;
     float M = -INFINITY;
 #pragma unroll
@@ -163,39 +192,99 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
       }
     }
   }
-  if (single) return;
+}
 
-  // ---- last workgroup of the unit combines the partials
-  __threadfence();
+// One workgroup per (sequence, KV head, query head of the group): merges the
+// unit's partials for that head.  Units handled by a single workgroup were
+// finished by the attention kernel.
+template <int D, bool DENSE>
+__global__ __launch_bounds__(256) void combine_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ counts,
+    uint16_t* __restrict__ out, int hq, int hkv, int per_wg, int wg_per_unit, int max_seq_len) {
+  constexpr int NQ = D / 4;            // float4 columns of one head
+  constexpr int PARTS = 256 / NQ;      // threads summing disjoint subsets of partials
+  __shared__ float sh_e[1024];
+  __shared__ float sh_red[256];
+  __shared__ float4 sh_acc[PARTS][NQ];
+  const int G = hq / hkv;
+  const int unit = blockIdx.x / G, h = blockIdx.x % G;
+  const int b = unit / hkv, g = unit % hkv;
+  const int L = min(seq_lens[b], max_seq_len);
+  const int n_items = DENSE ? (L + kPage - 1) / kPage : counts[2 * unit + 1];
+  const int n_wg = (n_items + per_wg - 1) / per_wg;
+  if (n_wg <= 1) return;
+  const int tid = threadIdx.x;
+  const float* ml = part_ml + 2 * (size_t)unit * wg_per_unit * G;
+
+  float m_loc = -INFINITY;
+  for (int w = tid; w < n_wg; w += 256) m_loc = fmaxf(m_loc, ml[2 * ((size_t)w * G + h)]);
+  sh_red[tid] = m_loc;
   __syncthreads();
-  if (threadIdx.x == 0) sh_last = (atomicAdd(&counters[unit], 1) == n_wg - 1);
-  __syncthreads();
-  if (!sh_last) return;
-  __threadfence();
-  const float* po0 = part_o + (size_t)unit * wg_per_unit * G * D;
-  const float* pml0 = part_ml + 2 * (size_t)unit * wg_per_unit * G;
-  for (int idx = threadIdx.x; idx < nout; idx += 256) {
-    const int h = idx / D, d = idx % D;
-    float M = -INFINITY;
-    for (int w = 0; w < n_wg; ++w) M = fmaxf(M, pml0[2 * ((size_t)w * G + h)]);
-    float o = 0.f, l = 0.f;
-    for (int w = 0; w < n_wg; ++w) {
-      const float e = exp2f(pml0[2 * ((size_t)w * G + h)] - M);
-      o += e * po0[(size_t)w * G * D + idx];
-      l += e * pml0[2 * ((size_t)w * G + h) + 1];
-    }
-    out[((size_t)b * hq + (size_t)g * G + h) * D + d] = (uint16_t)f32_to_bf16_bits(o / l);
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) sh_red[tid] = fmaxf(sh_red[tid], sh_red[tid + s]);
+    __syncthreads();
   }
-  if (threadIdx.x == 0) counters[unit] = 0;
+  const float M = sh_red[0];
+  __syncthreads();
+  float l_loc = 0.f;
+  for (int w = tid; w < n_wg; w += 256) {
+    const float e = exp2f(ml[2 * ((size_t)w * G + h)] - M);
+    sh_e[w] = e;
+    l_loc += e * ml[2 * ((size_t)w * G + h) + 1];
+  }
+  sh_red[tid] = l_loc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) sh_red[tid] += sh_red[tid + s];
+    __syncthreads();
+  }
+  const float Lsum = sh_red[0];
+
+  const int c4 = tid % NQ, part = tid / NQ;
+  const float4* po = reinterpret_cast<const float4*>(part_o + ((size_t)unit * wg_per_unit * G + h) * D) + c4;
+  const size_t wstride = (size_t)G * NQ;  // float4s between consecutive partials
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int w = part; w < n_wg; w += PARTS) {
+    const float e = sh_e[w];
+    const float4 v = po[(size_t)w * wstride];
+    a.x += e * v.x;
+    a.y += e * v.y;
+    a.z += e * v.z;
+    a.w += e * v.w;
+  }
+  sh_acc[part][c4] = a;
+  __syncthreads();
+  if (part == 0) {
+    for (int p = 1; p < PARTS; ++p) {
+      const float4 v = sh_acc[p][c4];
+      a.x += v.x;
+      a.y += v.y;
+      a.z += v.z;
+      a.w += v.w;
+    }
+    const float inv = 1.0f / Lsum;
+    const uint32_t w0 = f32_to_bf16_bits(a.x * inv) | (f32_to_bf16_bits(a.y * inv) << 16);
+    const uint32_t w1 = f32_to_bf16_bits(a.z * inv) | (f32_to_bf16_bits(a.w * inv) << 16);
+    *reinterpret_cast<uint2*>(out + ((size_t)b * hq + (size_t)g * G + h) * D + 4 * c4) = make_uint2(w0, w1);
+  }
 }
 
 }  // namespace
 
 AttnPlan plan_attention(int units, int max_items) {
-  AttnPlan p;
+  // one resident round of waves (3 workgroups of 4 waves per CU) shared out
+  // over all items; longer runs per wave when there is more work
+  static int res = 0;
+  if (res == 0) res = resident_blocks_per_cu(reinterpret_cast<const void*>(&decode_attention_kernel<128, false>), 256);
+  const long round_waves = (long)res * device_cu_count() * kAttnWaves;
   const long total = (long)units * max_items;
-  int ipw = 1;  // items per wave: at least ~4096 waves in flight, longer runs when work allows
-  while (ipw < 8 && total / (2 * ipw) >= 4096) ipw *= 2;
+  int ipw = (int)((total + round_waves - 1) / round_waves);
+  ipw = max(1, min(kMaxItemsPerWave, ipw));
+  // the combine keeps one weight per partial in LDS: at most 1024 partials per unit
+  while ((max_items + kAttnWaves * ipw - 1) / (kAttnWaves * ipw) > 1024) ++ipw;
+  AttnPlan p;
   p.items_per_wave = ipw;
   p.wg_per_unit = (max_items + kAttnWaves * ipw - 1) / (kAttnWaves * ipw);
   return p;
@@ -205,16 +294,23 @@ hipError_t launch_decode_attention(bool dense, const AttnPlan& plan, const uint1
                                    const uint16_t* kc, const uint16_t* vc,
                                    const int32_t* page_table, const int32_t* seq_lens,
                                    const int32_t* work, const int32_t* counts, float* part_o,
-                                   float* part_ml, int32_t* counters, uint16_t* out, int batch,
-                                   int hq, int hkv, int d, int max_pages, int max_items,
-                                   float sm_scale, int max_seq_len, hipStream_t stream) {
-  const dim3 grid((unsigned)((long)batch * hkv * plan.wg_per_unit));
+                                   float* part_ml, uint16_t* out, int batch, int hq, int hkv, int d,
+                                   int max_pages, int max_items, float sm_scale, int max_seq_len,
+                                   hipStream_t stream) {
+  const int units = batch * hkv;
+  const dim3 grid((unsigned)((long)units * plan.wg_per_unit));
   const float scale_log2 = sm_scale * 1.4426950408889634f;
-#define FSA_LAUNCH(DD, DN)                                                                        \
-  hipLaunchKernelGGL((decode_attention_kernel<DD, DN>), grid, dim3(256), 0, stream, q, kc, vc,   \
-                     page_table, seq_lens, work, counts, part_o, part_ml, counters, out, hq, hkv, \
-                     max_pages, max_items, plan.items_per_wave, plan.wg_per_unit, scale_log2,     \
-                     max_seq_len)
+#define FSA_LAUNCH(DD, DN)                                                                          \
+  do {                                                                                              \
+    hipLaunchKernelGGL((decode_attention_kernel<DD, DN>), grid, dim3(256), 0, stream, q, kc, vc,   \
+                       page_table, seq_lens, work, counts, part_o, part_ml, out, hq, hkv,          \
+                       max_pages, max_items, plan.items_per_wave, plan.wg_per_unit, scale_log2,     \
+                       max_seq_len);                                                                \
+    if (plan.wg_per_unit > 1)                                                                       \
+      hipLaunchKernelGGL((combine_kernel<DD, DN>), dim3((unsigned)(units * (hq / hkv))), dim3(256), \
+                         0, stream, part_o, part_ml, seq_lens, counts, out, hq, hkv,               \
+                         4 * plan.items_per_wave, plan.wg_per_unit, max_seq_len);                  \
+  } while (0)
   if (d == 128) {
     if (dense) FSA_LAUNCH(128, true); else FSA_LAUNCH(128, false);
   } else {

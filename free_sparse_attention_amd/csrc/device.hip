@@ -1,0 +1,28 @@
+// Device properties used to size grids: compute-unit count and how many
+// workgroups of a kernel fit on one compute unit.  Values are cached after
+// the first query (one device model per process is assumed).
+#include "fsa_internal.h"
+
+namespace fsa {
+
+int device_cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, c = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
+      n = c;
+    else
+      n = 256;  // MI355X
+  }
+  return n;
+}
+
+int resident_blocks_per_cu(const void* kernel, int block_threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block_threads, 0) != hipSuccess || n < 1)
+    n = 1;
+  return n;
+}
+
+}  // namespace fsa

@@ -41,6 +41,22 @@ __device__ __forceinline__ uint32_t f32_order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// ---------------------------------------------------------------- page metadata layout
+// Metadata is kept per (sequence b, KV head g, logical page p) -- it is derived
+// state of the sequence, so it needs no page-table lookup -- in tiles of 16
+// logical pages: tile t of unit (b, g) holds [2D/32 steps][16 pages][32 values],
+// where value e of page p is the minimum of key channel e (e < D) or the
+// maximum of channel e - D (e >= D).  One 16-page, 32-value slab is 1 KiB of
+// contiguous memory: exactly the operand that one MFMA step of the scoring
+// kernel loads.
+constexpr int kMetaTile = 16;
+__host__ __device__ inline int meta_tiles(int max_pages) { return (max_pages + kMetaTile - 1) / kMetaTile; }
+__host__ __device__ inline size_t meta_offset(int unit, int p, int e, int tiles, int D) {
+  const int ns = 2 * D / 32;
+  return (((size_t)unit * tiles + p / kMetaTile) * ns + e / 32) * (kMetaTile * 32) +
+         (size_t)(p % kMetaTile) * 32 + e % 32;
+}
+
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -53,6 +69,11 @@ __device__ __forceinline__ uint2 ld_nt(const uint2* p) {
   const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
   return make_uint2(v.x, v.y);
 }
+
+// ---------------------------------------------------------------- device
+
+int device_cu_count();
+int resident_blocks_per_cu(const void* kernel, int block_threads);
 
 // ---------------------------------------------------------------- launchers
 // All launchers enqueue on `stream` and return the launch status.
@@ -69,16 +90,18 @@ hipError_t launch_build_page_meta(const uint16_t* kc, const int32_t* page_table,
                                   const int32_t* seq_lens, uint16_t* meta, int batch, int hkv,
                                   int d, int max_pages, int max_seq_len, hipStream_t stream);
 
-hipError_t launch_quest_scores(const uint16_t* q, const uint16_t* meta, const int32_t* page_table,
-                               const int32_t* seq_lens, float* scores, int batch, int hq, int hkv,
-                               int d, int max_pages, int prefix, int window, int max_seq_len,
-                               hipStream_t stream);
+hipError_t launch_quest_scores(const uint16_t* q, const uint16_t* meta, const int32_t* seq_lens,
+                               float* scores, int batch, int hq, int hkv, int d, int max_pages,
+                               int prefix, int window, int max_seq_len, hipStream_t stream);
 
 hipError_t launch_select_pages(const float* scores, const int32_t* page_table,
                                const int32_t* seq_lens, int32_t* sel_pages, int32_t* work,
-                               int32_t* counts, int32_t* attn_counters, int batch, int hkv,
-                               int max_pages, int prefix, int window, int budget, int max_items,
-                               int max_seq_len, hipStream_t stream);
+                               int32_t* counts, int batch, int hkv, int max_pages, int prefix,
+                               int window, int budget, int max_items, int max_seq_len,
+                               hipStream_t stream);
+
+// Largest candidate count one selection workgroup holds.
+int select_max_candidates();
 
 struct AttnPlan {
   int items_per_wave;  // work items each wave walks through
@@ -91,8 +114,8 @@ hipError_t launch_decode_attention(bool dense, const AttnPlan& plan, const uint1
                                    const uint16_t* kc, const uint16_t* vc,
                                    const int32_t* page_table, const int32_t* seq_lens,
                                    const int32_t* work, const int32_t* counts, float* part_o,
-                                   float* part_ml, int32_t* counters, uint16_t* out, int batch,
-                                   int hq, int hkv, int d, int max_pages, int max_items,
-                                   float sm_scale, int max_seq_len, hipStream_t stream);
+                                   float* part_ml, uint16_t* out, int batch, int hq, int hkv, int d,
+                                   int max_pages, int max_items, float sm_scale, int max_seq_len,
+                                   hipStream_t stream);
 
 }  // namespace fsa

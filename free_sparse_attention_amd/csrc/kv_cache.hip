@@ -64,16 +64,24 @@ __device__ __forceinline__ void chunk_minmax(const uint4& kv, bool valid, uint32
   }
 }
 
-__device__ __forceinline__ void store_meta_chunk(uint16_t* mrow, int D, int c, const uint32_t mn[8],
-                                                 const uint32_t mx[8]) {
+// Metadata of channel chunk c (channels 8c .. 8c + 7) of logical page p of unit u.
+__device__ __forceinline__ uint4* meta_min_chunk(uint16_t* meta, int u, int p, int c, int tiles, int D) {
+  return reinterpret_cast<uint4*>(meta + meta_offset(u, p, 8 * c, tiles, D));
+}
+__device__ __forceinline__ uint4* meta_max_chunk(uint16_t* meta, int u, int p, int c, int tiles, int D) {
+  return reinterpret_cast<uint4*>(meta + meta_offset(u, p, D + 8 * c, tiles, D));
+}
+
+__device__ __forceinline__ void store_meta_chunk(uint16_t* meta, int u, int p, int c, int tiles, int D,
+                                                 const uint32_t mn[8], const uint32_t mx[8]) {
   uint32_t lo[4], hi[4];
 #pragma unroll
   for (int e = 0; e < 8; e += 2) {
     lo[e >> 1] = bf16_from_order_key(mn[e]) | (bf16_from_order_key(mn[e + 1]) << 16);
     hi[e >> 1] = bf16_from_order_key(mx[e]) | (bf16_from_order_key(mx[e + 1]) << 16);
   }
-  *reinterpret_cast<uint4*>(mrow + c * 8) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-  *reinterpret_cast<uint4*>(mrow + D + c * 8) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  *meta_min_chunk(meta, u, p, c, tiles, D) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  *meta_max_chunk(meta, u, p, c, tiles, D) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
 }
 
 // One wave per (sequence, KV head, touched page).  Lane (slot = lane % 16,
@@ -98,7 +106,7 @@ __global__ __launch_bounds__(64) void append_kv_kernel(
   const size_t blk = (size_t)page_table[(size_t)b * max_pages + p] * hkv + g;
   uint16_t* kdst = kc + blk * (kPage * D);
   uint16_t* vdst = vc + blk * (kPage * D);
-  uint16_t* mrow = meta + blk * (2 * D);
+  const int tiles = meta_tiles(max_pages);
   const bool valid = slot >= s0 && slot < s1;
 #pragma unroll
   for (int it = 0; it < NCH / 4; ++it) {
@@ -118,8 +126,8 @@ __global__ __launch_bounds__(64) void append_kv_kernel(
     chunk_minmax(kv, valid, mn, mx);
     if (slot == 0) {
       if (s0 > 0) {  // the page already holds tokens: merge with its metadata
-        const uint4 om = *reinterpret_cast<const uint4*>(mrow + c * 8);
-        const uint4 oM = *reinterpret_cast<const uint4*>(mrow + D + c * 8);
+        const uint4 om = *meta_min_chunk(meta, unit, p, c, tiles, D);
+        const uint4 oM = *meta_max_chunk(meta, unit, p, c, tiles, D);
         const uint32_t a[4] = {om.x, om.y, om.z, om.w}, z[4] = {oM.x, oM.y, oM.z, oM.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -127,7 +135,7 @@ __global__ __launch_bounds__(64) void append_kv_kernel(
           mx[e] = max(mx[e], bf16_order_key((z[e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
         }
       }
-      store_meta_chunk(mrow, D, c, mn, mx);
+      store_meta_chunk(meta, unit, p, c, tiles, D, mn, mx);
     }
   }
 }
@@ -150,14 +158,15 @@ __global__ __launch_bounds__(256) void build_page_meta_kernel(
   const int nvalid = min(kPage, L - p * kPage);
   const size_t blk = (size_t)page_table[(size_t)b * max_pages + p] * hkv + g;
   const uint16_t* ksrc = kc + blk * (kPage * D);
-  uint16_t* mrow = meta + blk * (2 * D);
+  const int tiles = meta_tiles(max_pages);
+  const int unit = b * hkv + g;
 #pragma unroll
   for (int it = 0; it < NCH / 4; ++it) {
     const int c = 4 * it + lane / kPage;
     const uint4 kv = *reinterpret_cast<const uint4*>(ksrc + (64 * it + lane) * 8);
     uint32_t mn[8], mx[8];
     chunk_minmax(kv, slot < nvalid, mn, mx);
-    if (slot == 0) store_meta_chunk(mrow, D, c, mn, mx);
+    if (slot == 0) store_meta_chunk(meta, unit, p, c, tiles, D, mn, mx);
   }
 }
 

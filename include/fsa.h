@@ -31,13 +31,23 @@
  *   k_cache     bf16  [pool][Hkv][D/8][S][8] K of token slot j, channel c of a page
  *                                           sits at [c/8][j][c%8]
  *   v_cache     bf16  [pool][Hkv][D][S]      V stored channel-major inside a page
- *   meta        bf16  [pool][Hkv][2][D]      [0] = elementwise min, [1] = max of the
- *                                           page's valid keys; a zero is stored as +0
+ *   meta        bf16  [B][Hkv][T][2D/32][16][32] with T = ceil(max_pages_per_seq / 16):
+ *                                           the elementwise min and max of the valid
+ *                                           keys of logical page p of sequence b, KV
+ *                                           head g, in tiles of 16 logical pages.
+ *                                           Value e of page p (e < D: min of channel e;
+ *                                           e >= D: max of channel e - D) sits at
+ *                                           [b][g][p / 16][e / 32][p % 16][e % 32].
+ *                                           A zero is stored as +0.  Size in bytes:
+ *                                           fsa_meta_bytes().
  *   page_table  int32 [B][max_pages_per_seq] logical page -> pool page
  *   seq_lens    int32 [B]                    tokens in the cache, including the
  *                                           current token (the query's position
  *                                           is seq_lens[b] - 1)
- * Supported: D in {64, 128}; S = 16; Hq / Hkv in 1..16; seq_lens[b] >= 1.
+ * Supported: D in {64, 128}; S = 16; Hq / Hkv in 1..16; seq_lens[b] >= 1;
+ * at most 32768 pages (512k tokens) per sequence.  max_seq_len arguments are
+ * host-side upper bounds of seq_lens used to size grids and workspaces;
+ * device lengths above the bound are clamped to it.
  */
 #ifndef FSA_H
 #define FSA_H
@@ -95,7 +105,7 @@ fsa_status fsa_import_kv_plain(const fsa_dims* dims, const void* k_plain, const 
  *   k_new, v_new  bf16 [B][n_new][Hkv][D] (device)
  *   seq_lens      int32 [B] (device), lengths before the append
  *   seq_lens_out  int32 [B] (device) or NULL; receives seq_lens[b] + n_new
- *                 (may alias seq_lens)
+ *                 (must not alias seq_lens)
  * A page whose slot 0 is written by this call gets fresh metadata from the
  * new tokens only; otherwise the new tokens' min/max are merged into the
  * existing entry.  The result equals fsa_build_page_meta bit for bit. */
@@ -105,9 +115,12 @@ fsa_status fsa_append_kv(const fsa_dims* dims, int32_t n_new, const void* k_new,
 
 /* Recompute the metadata of every page in use (logical pages
  * [0, ceil(seq_lens[b] / S)) of every sequence) from k_cache, over each
- * page's valid slots only.  Pool pages not in use are not written. */
+ * page's valid slots only.  Entries of pages not in use are not written. */
 fsa_status fsa_build_page_meta(const fsa_dims* dims, const void* k_cache, const int32_t* page_table,
                                const int32_t* seq_lens, void* meta, void* stream);
+
+/* Bytes of the page-metadata buffer for these dims (0 on invalid dims). */
+size_t fsa_meta_bytes(const fsa_dims* dims);
 
 /* Quest scores of the candidate pages.  For every (b, KV head g) and every
  * candidate logical page p:
@@ -118,8 +131,8 @@ fsa_status fsa_build_page_meta(const fsa_dims* dims, const void* k_cache, const 
  * non-candidate pages are not written.  max_seq_len is a host-side upper
  * bound of seq_lens used to size the grid. */
 fsa_status fsa_quest_scores(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len,
-                            const void* q, const void* meta, const int32_t* page_table,
-                            const int32_t* seq_lens, float* scores, void* stream);
+                            const void* q, const void* meta, const int32_t* seq_lens, float* scores,
+                            void* stream);
 
 /* Number of work items per (b, KV head) that fsa_select_pages can emit. */
 int32_t fsa_max_work_items(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len);
@@ -160,9 +173,8 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
 size_t fsa_dense_decode_workspace_bytes(const fsa_dims* dims, int32_t max_seq_len);
 
 /* Plain decode attention over all tokens [0, seq_lens[b]) with the same
- * split-K kernel: the baseline that the sparse step is measured against.
- * The workspace must be zero-filled before its first use; every call leaves
- * it ready for the next one. */
+ * split-K kernels: the baseline that the sparse step is measured against.
+ * The workspace needs no initial contents. */
 fsa_status fsa_dense_decode_attn(const fsa_dims* dims, float sm_scale, int32_t max_seq_len,
                                  const void* q, const void* k_cache, const void* v_cache,
                                  const int32_t* page_table, const int32_t* seq_lens, void* out,

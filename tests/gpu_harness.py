@@ -46,10 +46,19 @@ class DeviceWorkload:
         self.v_cache = torch.empty_like(vp)
         fsa.import_kv_plain(self.dims, kp, vp, self.k_cache, self.v_cache)
         del kp, vp
-        self.meta = torch.zeros((wl.pool_pages, wl.hkv, 2, wl.d), dtype=torch.bfloat16, device=device)
+        self.meta = torch.zeros(fsa.meta_bytes(self.dims) // 2, dtype=torch.bfloat16, device=device)
         if build_meta:
             fsa.build_page_meta(self.dims, self.k_cache, self.page_table, self.seq_lens, self.meta)
         torch.cuda.synchronize()
+
+    def meta_pages(self, meta=None) -> np.ndarray:
+        """Library metadata as bf16 bits [B][Hkv][max_pages][2][D] (index 0 = min, 1 = max)."""
+        wl = self.wl
+        T = -(-wl.max_pages // 16)
+        ns = 2 * wl.d // 32
+        m = bits(self.meta if meta is None else meta).reshape(wl.batch, wl.hkv, T, ns, 16, 32)
+        m = m.transpose(0, 1, 2, 4, 3, 5).reshape(wl.batch, wl.hkv, T * 16, 2 * wl.d)[:, :, :wl.max_pages]
+        return m.reshape(wl.batch, wl.hkv, wl.max_pages, 2, wl.d)
 
     # ------------------------------------------------------------ entry points
     def cfg(self, cfg=None):
@@ -59,7 +68,7 @@ class DeviceWorkload:
         wl = self.wl
         s = torch.full((wl.batch, wl.hkv, wl.max_pages), float("nan"), dtype=torch.float32, device=self.device)
         fsa.quest_scores(self.dims, self.cfg(cfg), max_seq_len or self.max_seq_len, self.q if q is None else q,
-                         self.meta, self.page_table, self.seq_lens, s)
+                         self.meta, self.seq_lens, s)
         return s
 
     def select(self, scores, cfg=None, max_seq_len=None):

@@ -45,6 +45,7 @@ def test_workspace_sizing_and_bad_shapes(lib):
     assert fsa.sparse_decode_workspace_bytes(_d(), c, 4096) > 0
     assert fsa.dense_decode_workspace_bytes(_d(), 4096) > 0
     assert fsa.max_work_items(_d(), c, 4096) == 4 + 32 + 17
+    assert fsa.meta_bytes(_d()) == 1 * 2 * 16 * 16 * 2 * 64 * 2
     for bad, status in ((dict(head_dim=96), _lib.FSA_ERR_UNSUPPORTED), (dict(num_q_heads=7), _lib.FSA_ERR_INVALID_ARG),
                         (dict(num_q_heads=34, num_kv_heads=2), _lib.FSA_ERR_UNSUPPORTED),
                         (dict(batch=0), _lib.FSA_ERR_INVALID_ARG)):
@@ -52,7 +53,7 @@ def test_workspace_sizing_and_bad_shapes(lib):
         with pytest.raises(fsa.FsaError) as e:
             fsa.sparse_decode_workspace_bytes(_d(**bad), c, 4096)
         assert "dims" in str(e.value)
-        st = lib.fsa_quest_scores(ctypes.byref(_d(**bad)), c, 4096, None, None, None, None, None, None)
+        st = lib.fsa_quest_scores(ctypes.byref(_d(**bad)), c, 4096, None, None, None, None, None)
         assert st == status
     # page size other than 16
     assert lib.fsa_build_page_meta(ctypes.byref(_d(page_size=32)), None, None, None, None, None) == _lib.FSA_ERR_UNSUPPORTED
@@ -61,11 +62,11 @@ def test_workspace_sizing_and_bad_shapes(lib):
 def test_bad_cfg_len_and_pointers(lib):
     d = _d()
     p = ctypes.c_void_p(16)  # never dereferenced: every check runs before a launch
-    assert lib.fsa_quest_scores(ctypes.byref(d), fsa.cfg(0, 0, 0), 4096, p, p, p, p, p, None) == _lib.FSA_ERR_INVALID_ARG
+    assert lib.fsa_quest_scores(ctypes.byref(d), fsa.cfg(0, 0, 0), 4096, p, p, p, p, None) == _lib.FSA_ERR_INVALID_ARG
     assert b"attends to nothing" in lib.fsa_last_error()
-    assert lib.fsa_quest_scores(ctypes.byref(d), fsa.cfg(-1, 0, 4), 4096, p, p, p, p, p, None) == _lib.FSA_ERR_INVALID_ARG
-    assert lib.fsa_quest_scores(ctypes.byref(d), fsa.cfg(64, 256, 32), 4097, p, p, p, p, p, None) == _lib.FSA_ERR_INVALID_ARG
-    assert lib.fsa_quest_scores(ctypes.byref(d), fsa.cfg(64, 256, 32), 4096, p, None, p, p, p, None) == _lib.FSA_ERR_INVALID_ARG
+    assert lib.fsa_quest_scores(ctypes.byref(d), fsa.cfg(-1, 0, 4), 4096, p, p, p, p, None) == _lib.FSA_ERR_INVALID_ARG
+    assert lib.fsa_quest_scores(ctypes.byref(d), fsa.cfg(64, 256, 32), 4097, p, p, p, p, None) == _lib.FSA_ERR_INVALID_ARG
+    assert lib.fsa_quest_scores(ctypes.byref(d), fsa.cfg(64, 256, 32), 4096, p, None, p, p, None) == _lib.FSA_ERR_INVALID_ARG
     assert b"meta" in lib.fsa_last_error()
     assert lib.fsa_append_kv(ctypes.byref(d), 0, p, p, p, p, None, p, p, p, None) == _lib.FSA_ERR_INVALID_ARG
     assert lib.fsa_append_kv(ctypes.byref(d), 1, p, p, p, p, p, p, p, p, None) == _lib.FSA_ERR_INVALID_ARG

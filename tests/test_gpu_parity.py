@@ -50,15 +50,15 @@ def meta_bits_oracle(K, L):
 
 def check_meta(dw, units=None):
     wl = dw.wl
-    meta = bits(dw.meta)  # [pool][hkv][2][D]
+    meta = dw.meta_pages()  # [B][hkv][max_pages][2][D]
     units = units or [(b, g) for b in range(wl.batch) for g in range(wl.hkv)]
     for b, g in units:
         L = int(wl.seq_lens[b])
         K = oracle.gather_keys(wl.k_pool, wl.page_table, b, g, L)
         mo, Mo = meta_bits_oracle(K, L)
-        phys = wl.page_table[b, :mo.shape[0]]
-        assert np.array_equal(meta[phys, g, 0], mo), f"meta min differs, unit {(b, g)}"
-        assert np.array_equal(meta[phys, g, 1], Mo), f"meta max differs, unit {(b, g)}"
+        n = mo.shape[0]
+        assert np.array_equal(meta[b, g, :n, 0], mo), f"meta min differs, unit {(b, g)}"
+        assert np.array_equal(meta[b, g, :n, 1], Mo), f"meta max differs, unit {(b, g)}"
 
 
 def check_selection(sel_gpu, ora, budget):
@@ -244,10 +244,10 @@ def test_append_matches_rebuild_and_oracle():
         dw.seq_lens = lens
         fsa.build_page_meta(dw.dims, dw.k_cache, dw.page_table, lens, rebuilt)
         torch.cuda.synchronize()
-        mb, rb = bits(dw.meta), bits(rebuilt)
+        mb, rb = dw.meta_pages(), dw.meta_pages(rebuilt)
         for b in range(wl.batch):
-            used = wl.page_table[b, :-(-int(wl.seq_lens[b]) // S)]
-            assert np.array_equal(mb[used], rb[used]), f"append vs rebuild, seq {b}"
+            n = -(-int(wl.seq_lens[b]) // S)
+            assert np.array_equal(mb[b, :, :n], rb[b, :, :n]), f"append vs rebuild, seq {b}"
     dw.max_seq_len = int(wl.seq_lens.max())
     # the converted caches equal a fresh import of the oracle's plain pool
     fresh = DeviceWorkload(wl)
