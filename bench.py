@@ -58,6 +58,20 @@ def alg_bytes(wl):
     return score, step
 
 
+def measured_traffic(kernel_source: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None when
+    the kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "quest_score_%s_counters.json" % workload)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, kernel_source), "rb").read()
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """The CPU oracle timed on host cores over a bounded sample of units of the same workload."""
     import oracle
@@ -215,7 +229,8 @@ def main():
         "speedup_vs_dense": r.get("speedup_vs_dense"),
         "roofline": {"bound": "hbm", "kernel": "quest_score_kernel", "achieved": r["score_GBps"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": r["score_GBps"] / HBM_PEAK_GBS,
-                     "traffic": None, "avg_launch_us": 1000.0 * r["score_ms"],
+                     "traffic": measured_traffic("free_sparse_attention_amd/csrc/quest_score.hip", args.workload),
+                     "avg_launch_us": 1000.0 * r["score_ms"],
                      "alg_bytes_per_launch": r["score_alg_bytes"]},
         "cpu_baseline": cpu,
         "also": {k: {"steps_per_s": v["steps_per_s"], "ms_per_step": v["ms_per_step"],
