@@ -133,6 +133,32 @@ DenseWs dense_ws(const fsa_dims* d, int32_t max_seq_len) {
   return w;
 }
 
+fsa::AttnArgs attn_args(const fsa_dims* dims, int max_items, float sm_scale, int32_t max_seq_len,
+                        const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* page_table, const int32_t* seq_lens, const int32_t* work,
+                        const int32_t* counts, float* part_o, float* part_ml, void* out) {
+  fsa::AttnArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kc = static_cast<const uint16_t*>(k_cache);
+  a.vc = static_cast<const uint16_t*>(v_cache);
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.work = work;
+  a.counts = counts;
+  a.part_o = part_o;
+  a.part_ml = part_ml;
+  a.out = static_cast<uint16_t*>(out);
+  a.batch = dims->batch;
+  a.hq = dims->num_q_heads;
+  a.hkv = dims->num_kv_heads;
+  a.d = dims->head_dim;
+  a.max_pages = dims->max_pages_per_seq;
+  a.max_items = max_items;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.max_seq_len = max_seq_len;
+  return a;
+}
+
 template <typename T>
 T* at(void* base, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(base) + off);
@@ -282,21 +308,15 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
   FSA_CHECK(hip_status(
       fsa::launch_select_pages(at<float>(workspace, w.scores), page_table, seq_lens, sel_pages,
                                at<int32_t>(workspace, w.work), at<int32_t>(workspace, w.counts),
-                               dims->batch, dims->num_kv_heads,
-                               dims->max_pages_per_seq, cfg.prefix_tokens, cfg.window_tokens,
-                               cfg.budget_pages, w.max_items, max_seq_len, st),
+                               dims->batch, dims->num_kv_heads, dims->max_pages_per_seq,
+                               cfg.prefix_tokens, cfg.window_tokens, cfg.budget_pages, w.max_items,
+                               max_seq_len, st),
       "select_pages launch"));
-  return hip_status(
-      fsa::launch_decode_attention(false, w.plan, static_cast<const uint16_t*>(q),
-                                   static_cast<const uint16_t*>(k_cache),
-                                   static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
-                                   at<int32_t>(workspace, w.work), at<int32_t>(workspace, w.counts),
-                                   at<float>(workspace, w.part_o), at<float>(workspace, w.part_ml),
-                                   static_cast<uint16_t*>(out),
-                                   dims->batch, dims->num_q_heads, dims->num_kv_heads,
-                                   dims->head_dim, dims->max_pages_per_seq, w.max_items, sm_scale, max_seq_len,
-                                   st),
-      "decode_attention launch");
+  const fsa::AttnArgs a = attn_args(dims, w.max_items, sm_scale, max_seq_len, q, k_cache, v_cache,
+                                    page_table, seq_lens, at<int32_t>(workspace, w.work),
+                                    at<int32_t>(workspace, w.counts), at<float>(workspace, w.part_o),
+                                    at<float>(workspace, w.part_ml), out);
+  return hip_status(fsa::launch_attention(fsa::kList, w.plan, a, st), "decode attention launch");
 }
 
 size_t fsa_dense_decode_workspace_bytes(const fsa_dims* dims, int32_t max_seq_len) {
@@ -320,16 +340,11 @@ fsa_status fsa_dense_decode_attn(const fsa_dims* dims, float sm_scale, int32_t m
   const DenseWs w = dense_ws(dims, max_seq_len);
   if (!workspace || workspace_bytes < w.total)
     return fail(FSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, w.total);
-  return hip_status(
-      fsa::launch_decode_attention(true, w.plan, static_cast<const uint16_t*>(q),
-                                   static_cast<const uint16_t*>(k_cache),
-                                   static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
-                                   nullptr, nullptr, at<float>(workspace, w.part_o),
-                                   at<float>(workspace, w.part_ml), static_cast<uint16_t*>(out),
-                                   dims->batch, dims->num_q_heads, dims->num_kv_heads,
-                                   dims->head_dim, dims->max_pages_per_seq, w.max_items, sm_scale,
-                                   max_seq_len, static_cast<hipStream_t>(stream)),
-      "dense decode_attention launch");
+  const fsa::AttnArgs a = attn_args(dims, w.max_items, sm_scale, max_seq_len, q, k_cache, v_cache,
+                                    page_table, seq_lens, nullptr, nullptr, at<float>(workspace, w.part_o),
+                                    at<float>(workspace, w.part_ml), out);
+  return hip_status(fsa::launch_attention(fsa::kDense, w.plan, a, static_cast<hipStream_t>(stream)),
+                    "dense decode attention launch");
 }
 
 }  // extern "C"

@@ -1,4 +1,4 @@
-// Split-K flash decoding over the attended pages, then the cross-split combine.
+// Split-K flash decoding over attended pages, then the cross-split combine.
 //
 // Per work item (one page, a token range [lo, hi) inside it), one wave:
 //   S^T[token][head] = K[token][:] . q[head][:]     v_mfma_f32_16x16x32_bf16, D/32 steps
@@ -13,10 +13,15 @@
 // walks a run of items with the next page's loads in flight while the current
 // page is computed.
 //
-// Four waves per workgroup; the workgroup merges its waves' (max, sum,
-// accumulator) through LDS and writes one partial (or the final output when
-// the unit has a single workgroup).  A second kernel combines partials:
+// Items come either from the selection's work list (prefix, selected and
+// window pages; kList) or are every page of the sequence (kDense, the dense
+// baseline).  Four waves per workgroup; the workgroup merges its waves' (max,
+// sum, accumulator) through LDS and writes one partial into its slot, or the
+// output directly when a unit needs a single workgroup.  The combine kernel
+// merges a unit's partials:
 //   o = sum_j 2^(m_j - m) o_j / sum_j 2^(m_j - m) l_j,  m = max_j m_j.
+#include <algorithm>
+
 #include "fsa_internal.h"
 
 namespace fsa {
@@ -28,7 +33,7 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int wave_bcast(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 
-template <int D, bool DENSE>
+template <int D, int MODE>
 __global__ __launch_bounds__(256, 3) void decode_attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ page_table,
@@ -46,7 +51,7 @@ __global__ __launch_bounds__(256, 3) void decode_attention_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, gq = lane >> 4;
   const int L = min(seq_lens[b], max_seq_len);  // lengths beyond the host bound are clamped
-  const int n_items = DENSE ? (L + kPage - 1) / kPage : counts[2 * unit + 1];
+  const int n_items = MODE == kDense ? (L + kPage - 1) / kPage : counts[2 * unit + 1];
   const int per_wg = kAttnWaves * ipw;
   const int n_wg = (n_items + per_wg - 1) / per_wg;
   if (wg >= n_wg) return;
@@ -58,7 +63,7 @@ __global__ __launch_bounds__(256, 3) void decode_attention_kernel(
   int my_phys = 0, my_lo = 0, my_hi = 0;
   if (lane < n) {
     const int i = i_begin + lane;
-    if (DENSE) {
+    if (MODE == kDense) {
       my_phys = pt[i];
       my_hi = min(kPage, L - i * kPage);
     } else {
@@ -167,9 +172,10 @@ __global__ __launch_bounds__(256, 3) void decode_attention_kernel(
     for (int r = 0; r < 4; ++r) sh_o[wave][16 * t + 4 * gq + r][col] = acc[t][r];
   __syncthreads();
 
-  const bool single = (n_wg == 1);
-  float* po = part_o + ((size_t)unit * wg_per_unit + wg) * G * D;
-  float* pml = part_ml + 2 * ((size_t)unit * wg_per_unit + wg) * G;
+  const bool direct = n_wg == 1;
+  const size_t slot = (size_t)unit * wg_per_unit + wg;
+  float* po = part_o + slot * G * D;
+  float* pml = part_ml + 2 * slot * G;
   for (int idx = threadIdx.x; idx < G * D; idx += 256) {
     const int h = idx / D, d = idx % D;
     float M = -INFINITY;
@@ -182,7 +188,7 @@ __global__ __launch_bounds__(256, 3) void decode_attention_kernel(
       o += e * sh_o[w][d][h];
       l += e * sh_l[w][h];
     }
-    if (single) {
+    if (direct) {
       out[((size_t)b * hq + (size_t)g * G + h) * D + d] = (uint16_t)f32_to_bf16_bits(o / l);
     } else {
       po[idx] = o;
@@ -196,57 +202,49 @@ __global__ __launch_bounds__(256, 3) void decode_attention_kernel(
 
 // One workgroup per (sequence, KV head, query head of the group): merges the
 // unit's partials for that head.  Units handled by a single workgroup were
-// finished by the attention kernel.
-template <int D, bool DENSE>
+// finished by the attention kernel.  Every wave redundantly reduces the
+// partials' maxima and sums (no barrier); the 256 threads then sum float4
+// columns over disjoint subsets of partials and merge them in LDS.
+template <int D, int MODE>
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ counts,
     uint16_t* __restrict__ out, int hq, int hkv, int per_wg, int wg_per_unit, int max_seq_len) {
   constexpr int NQ = D / 4;            // float4 columns of one head
   constexpr int PARTS = 256 / NQ;      // threads summing disjoint subsets of partials
-  __shared__ float sh_e[1024];
-  __shared__ float sh_red[256];
+  __shared__ float sh_e[kMaxPartials];
   __shared__ float4 sh_acc[PARTS][NQ];
   const int G = hq / hkv;
   const int unit = blockIdx.x / G, h = blockIdx.x % G;
   const int b = unit / hkv, g = unit % hkv;
   const int L = min(seq_lens[b], max_seq_len);
-  const int n_items = DENSE ? (L + kPage - 1) / kPage : counts[2 * unit + 1];
-  const int n_wg = (n_items + per_wg - 1) / per_wg;
-  if (n_wg <= 1) return;
-  const int tid = threadIdx.x;
+  const int n_items = MODE == kDense ? (L + kPage - 1) / kPage : counts[2 * unit + 1];
+  const int n = (n_items + per_wg - 1) / per_wg;
+  if (n <= 1) return;  // written directly by the attention kernel
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* ml = part_ml + 2 * (size_t)unit * wg_per_unit * G;
 
-  float m_loc = -INFINITY;
-  for (int w = tid; w < n_wg; w += 256) m_loc = fmaxf(m_loc, ml[2 * ((size_t)w * G + h)]);
-  sh_red[tid] = m_loc;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) sh_red[tid] = fmaxf(sh_red[tid], sh_red[tid + s]);
-    __syncthreads();
-  }
-  const float M = sh_red[0];
-  __syncthreads();
+  float M = -INFINITY;
+  for (int w = lane; w < n; w += kWave) M = fmaxf(M, ml[2 * ((size_t)w * G + h)]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float l_loc = 0.f;
-  for (int w = tid; w < n_wg; w += 256) {
+  for (int w = lane; w < n; w += kWave) {
     const float e = exp2f(ml[2 * ((size_t)w * G + h)] - M);
-    sh_e[w] = e;
+    if (wave == 0) sh_e[w] = e;
     l_loc += e * ml[2 * ((size_t)w * G + h) + 1];
   }
-  sh_red[tid] = l_loc;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) l_loc += __shfl_xor(l_loc, off);
+  const float Lsum = l_loc;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) sh_red[tid] += sh_red[tid + s];
-    __syncthreads();
-  }
-  const float Lsum = sh_red[0];
 
   const int c4 = tid % NQ, part = tid / NQ;
   const float4* po = reinterpret_cast<const float4*>(part_o + ((size_t)unit * wg_per_unit * G + h) * D) + c4;
   const size_t wstride = (size_t)G * NQ;  // float4s between consecutive partials
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
-  for (int w = part; w < n_wg; w += PARTS) {
+  for (int w = part; w < n; w += PARTS) {
     const float e = sh_e[w];
     const float4 v = po[(size_t)w * wstride];
     a.x += e * v.x;
@@ -277,46 +275,40 @@ AttnPlan plan_attention(int units, int max_items) {
   // one resident round of waves (3 workgroups of 4 waves per CU) shared out
   // over all items; longer runs per wave when there is more work
   static int res = 0;
-  if (res == 0) res = resident_blocks_per_cu(reinterpret_cast<const void*>(&decode_attention_kernel<128, false>), 256);
+  if (res == 0)
+    res = resident_blocks_per_cu(reinterpret_cast<const void*>(&decode_attention_kernel<128, kList>), 256);
   const long round_waves = (long)res * device_cu_count() * kAttnWaves;
-  const long total = (long)units * max_items;
+  const long total = (long)units * std::max(1, max_items);
   int ipw = (int)((total + round_waves - 1) / round_waves);
   ipw = max(1, min(kMaxItemsPerWave, ipw));
-  // the combine keeps one weight per partial in LDS: at most 1024 partials per unit
-  while ((max_items + kAttnWaves * ipw - 1) / (kAttnWaves * ipw) > 1024) ++ipw;
+  // the combine keeps one weight per partial in LDS
+  while ((max_items + kAttnWaves * ipw - 1) / (kAttnWaves * ipw) > kMaxPartials) ++ipw;
   AttnPlan p;
   p.items_per_wave = ipw;
-  p.wg_per_unit = (max_items + kAttnWaves * ipw - 1) / (kAttnWaves * ipw);
+  p.wg_per_unit = std::max(1, (max_items + kAttnWaves * ipw - 1) / (kAttnWaves * ipw));
   return p;
 }
 
-hipError_t launch_decode_attention(bool dense, const AttnPlan& plan, const uint16_t* q,
-                                   const uint16_t* kc, const uint16_t* vc,
-                                   const int32_t* page_table, const int32_t* seq_lens,
-                                   const int32_t* work, const int32_t* counts, float* part_o,
-                                   float* part_ml, uint16_t* out, int batch, int hq, int hkv, int d,
-                                   int max_pages, int max_items, float sm_scale, int max_seq_len,
-                                   hipStream_t stream) {
-  const int units = batch * hkv;
-  const dim3 grid((unsigned)((long)units * plan.wg_per_unit));
-  const float scale_log2 = sm_scale * 1.4426950408889634f;
-#define FSA_LAUNCH(DD, DN)                                                                          \
-  do {                                                                                              \
-    hipLaunchKernelGGL((decode_attention_kernel<DD, DN>), grid, dim3(256), 0, stream, q, kc, vc,   \
-                       page_table, seq_lens, work, counts, part_o, part_ml, out, hq, hkv,          \
-                       max_pages, max_items, plan.items_per_wave, plan.wg_per_unit, scale_log2,     \
-                       max_seq_len);                                                                \
-    if (plan.wg_per_unit > 1)                                                                       \
-      hipLaunchKernelGGL((combine_kernel<DD, DN>), dim3((unsigned)(units * (hq / hkv))), dim3(256), \
-                         0, stream, part_o, part_ml, seq_lens, counts, out, hq, hkv,               \
-                         4 * plan.items_per_wave, plan.wg_per_unit, max_seq_len);                  \
+hipError_t launch_attention(AttnMode mode, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
+  const unsigned units = (unsigned)(a.batch * a.hkv);
+  const dim3 grid(units * (unsigned)plan.wg_per_unit);
+#define FSA_ATTN(DD, MM)                                                                              \
+  do {                                                                                                \
+    hipLaunchKernelGGL((decode_attention_kernel<DD, MM>), grid, dim3(256), 0, stream, a.q, a.kc, a.vc,  \
+                       a.page_table, a.seq_lens, a.work, a.counts, a.part_o, a.part_ml, a.out, a.hq,   \
+                       a.hkv, a.max_pages, a.max_items, plan.items_per_wave, plan.wg_per_unit,        \
+                       a.scale_log2, a.max_seq_len);                                                   \
+    if (plan.wg_per_unit > 1)                                                                         \
+      hipLaunchKernelGGL((combine_kernel<DD, MM>), dim3((unsigned)(a.batch * a.hq)), dim3(256), 0,     \
+                         stream, a.part_o, a.part_ml, a.seq_lens, a.counts, a.out, a.hq, a.hkv,        \
+                         kAttnWaves * plan.items_per_wave, plan.wg_per_unit, a.max_seq_len);           \
   } while (0)
-  if (d == 128) {
-    if (dense) FSA_LAUNCH(128, true); else FSA_LAUNCH(128, false);
+  if (a.d == 128) {
+    if (mode == kDense) FSA_ATTN(128, kDense); else FSA_ATTN(128, kList);
   } else {
-    if (dense) FSA_LAUNCH(64, true); else FSA_LAUNCH(64, false);
+    if (mode == kDense) FSA_ATTN(64, kDense); else FSA_ATTN(64, kList);
   }
-#undef FSA_LAUNCH
+#undef FSA_ATTN
   return hipGetLastError();
 }
 

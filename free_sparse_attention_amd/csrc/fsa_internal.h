@@ -57,6 +57,39 @@ __host__ __device__ inline size_t meta_offset(int unit, int p, int e, int tiles,
          (size_t)(p % kMetaTile) * 32 + e % 32;
 }
 
+// ---------------------------------------------------------------- wave-level DPP primitives
+// Inclusive prefix sum over the 64 lanes of a wave: row shifts within each
+// 16-lane row, then row broadcasts of lanes 15 and 31 across rows.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+// Wave-wide minimum and maximum (every lane receives the result).
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+  const uint32_t id = 0xFFFFFFFFu;
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x111, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x112, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x114, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x118, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x142, 0xa, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -108,14 +141,31 @@ struct AttnPlan {
   int wg_per_unit;     // workgroups launched per (b, KV head)
 };
 
+// Attention work-item sources: every page of the sequence, or the selection's work list.
+enum AttnMode { kDense = 0, kList = 1 };
+constexpr int kMaxPartials = 1024;  // partial results per unit the combine can merge
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* work;    // selection work items (kList)
+  const int32_t* counts;  // (k, items) per unit (kList)
+  float* part_o;
+  float* part_ml;
+  uint16_t* out;
+  int batch, hq, hkv, d, max_pages, max_items;
+  float scale_log2;
+  int max_seq_len;
+};
+
+// Plan for `max_items` items per unit (at most kMaxPartials workgroups per unit).
 AttnPlan plan_attention(int units, int max_items);
 
-hipError_t launch_decode_attention(bool dense, const AttnPlan& plan, const uint16_t* q,
-                                   const uint16_t* kc, const uint16_t* vc,
-                                   const int32_t* page_table, const int32_t* seq_lens,
-                                   const int32_t* work, const int32_t* counts, float* part_o,
-                                   float* part_ml, uint16_t* out, int batch, int hq, int hkv, int d,
-                                   int max_pages, int max_items, float sm_scale, int max_seq_len,
-                                   hipStream_t stream);
+// Split-K attention over the unit's items, then (when a unit can need more
+// than one workgroup) the combine of its partials.
+hipError_t launch_attention(AttnMode mode, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
 
 }  // namespace fsa

@@ -4,23 +4,26 @@
 // a fixed budget of query-aware top-k pages next to the prefix and the
 // window.  Here, per (sequence, KV head), one workgroup of 1024 threads:
 //   1. loads the candidates' scores as order-preserving 32-bit keys into LDS
-//      (128 KiB: up to 32768 candidates); thread t of the block handles
-//      candidates t, t + 1024, ... so every load instruction reads 256
-//      contiguous bytes and LDS accesses are bank-conflict free;
+//      (128 KiB: up to 32768 candidates) and their page-table entries into
+//      registers; thread t handles candidates t, t + 1024, ... so every load
+//      instruction reads 256 contiguous bytes and LDS accesses are
+//      bank-conflict free;
 //   2. finds the k-th largest key exactly by most-significant-digit radix
 //      select.  Digits start right below the bits that the smallest and the
-//      largest key share, 11 bits at a time (2048 LDS bins), so the first
-//      histogram already spreads the scores; a wave-level scan locates the
-//      digit holding the k-th key, and the search stops as soon as that
-//      digit's bin holds exactly the number of keys still needed;
-//   3. ranks the selected pages in ascending id order from per-wave ballots:
-//      a candidate's rank among the keys tied with the threshold (ties go to
-//      the lower page id) and its output slot are a popcount within its wave
-//      plus a prefix over (column, wave) counts;
+//      largest key share, 11 bits at a time (2048 LDS bins, double-buffered
+//      so a pass costs two barriers), so the first histogram already spreads
+//      the scores; a wave-level scan locates the digit holding the k-th key,
+//      and the search stops as soon as that digit's bin holds exactly the
+//      number of keys still needed;
+//   3. turns per-wave ballots ("above the threshold", "tied with it") into
+//      id-ordered bitmaps; block-wide prefix sums of their popcounts take the
+//      tied pages in id order (ties go to the lower page id) and give every
+//      selected page its output slot, so pages come out ascending;
 //   4. writes the attended tokens as work items.  The attended set is split
 //      into three disjoint token ranges -- prefix [0, Pe), the middle tokens
 //      [Pe, Ws) of selected pages and the window [max(Ws, Pe), L) -- so no
 //      token appears twice and no sort or dedup pass is needed.
+// Wave-level scans and reductions use DPP row operations.
 #include "fsa_internal.h"
 
 namespace fsa {
@@ -28,16 +31,24 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kCols = 32;  // keys per thread: up to 32768 candidate pages (512k tokens)
+constexpr int kCols = 32;  // candidates per thread: up to 32768 (512k tokens)
 constexpr int kMaxCand = kSelThreads * kCols;
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
 
 __device__ __forceinline__ int popc64(unsigned long long x) { return __popcll(x); }
 
-__device__ __forceinline__ unsigned long long lanes_below() {
-  const int lane = threadIdx.x & 63;
-  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+// Exclusive prefix sum of one int per thread over the 1024-thread block.
+__device__ __forceinline__ int block_excl_sum(int v, int* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = (int)wave_incl_sum((uint32_t)v);
+  if (lane == kWave - 1) sh[wave] = incl;
+  __syncthreads();
+  int base = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) base += (w < wave) ? sh[w] : 0;
+  __syncthreads();
+  return base + incl - v;
 }
 
 __device__ __forceinline__ void put_item(int32_t* work, int idx, int p, int phys, int lo, int hi) {
@@ -50,9 +61,10 @@ __global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
     int32_t* __restrict__ work, int32_t* __restrict__ counts, int hkv, int max_pages, int prefix,
     int window, int budget, int max_items, int max_seq_len) {
   __shared__ uint32_t skey[kMaxCand];
-  __shared__ uint32_t hist[kBins];
-  __shared__ int cnt_a[kCols][kSelWaves];  // per (column, wave): keys above the threshold, then output base
-  __shared__ int cnt_e[kCols][kSelWaves];  // per (column, wave): keys tied with it, then tie-rank base
+  __shared__ uint32_t hist[2][kBins];
+  __shared__ unsigned long long bm_gt[kCols * kSelWaves];  // id-ordered bitmap: key above the threshold
+  __shared__ unsigned long long bm_eq[kCols * kSelWaves];  // id-ordered bitmap: key tied with it
+  __shared__ int scan_sh[kSelWaves + 1];
   __shared__ uint32_t mm_sh[2 * kSelWaves];
   __shared__ uint32_t s_prefix, s_need, s_done;
 
@@ -68,31 +80,43 @@ __global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
   const int cols = (C + kSelThreads - 1) / kSelThreads;  // uniform
   const float* sc = scores + (size_t)unit * max_pages + c_lo;
   const int32_t* pt = page_table + (size_t)b * max_pages;
+  const int32_t* ptc = pt + c_lo;
 
-  // ---- 1. keys: candidate i = tid + 1024 j in skey[i]
+  // ---- 1. keys (LDS) and page-table entries (registers) of candidates tid + 1024 j;
+  // every load is issued before the first one is used
+  int phys[kCols];
+  uint32_t raw[kCols];
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   if (radix) {
-#pragma unroll 8
-    for (int j = 0; j < cols; ++j) {
-      const int i = tid + kSelThreads * j;
-      const uint32_t key = f32_order_key(sc[min(i, C - 1)]);
-      skey[i] = key;
-      if (i < C) {
-        kmin = min(kmin, key);
-        kmax = max(kmax, key);
+#pragma unroll
+    for (int j = 0; j < kCols; ++j) {
+      if (j < cols) {
+        const int ic = min(tid + kSelThreads * j, C - 1);
+        raw[j] = __float_as_uint(sc[ic]);
+        phys[j] = ptc[ic];
       }
     }
+#pragma unroll
+    for (int j = 0; j < kCols; ++j) {
+      if (j < cols) {
+        const int i = tid + kSelThreads * j;
+        const uint32_t key = f32_order_key(__uint_as_float(raw[j]));
+        skey[i] = key;
+        if (i < C) {
+          kmin = min(kmin, key);
+          kmax = max(kmax, key);
+        }
+      }
+    }
+    for (int i = tid; i < kBins; i += kSelThreads) hist[0][i] = 0;
   }
 
   // ---- 2. exact k-th largest key: keys >> shift compared with kprefix, `need` ties to take
   uint32_t kprefix = 0, need = (uint32_t)k;
   int shift = 0;
   if (radix) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
-      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
-    }
+    kmin = wave_min(kmin);
+    kmax = wave_max(kmax);
     if (lane == 0) {
       mm_sh[2 * wave] = kmin;
       mm_sh[2 * wave + 1] = kmax;
@@ -109,42 +133,32 @@ __global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
     } else {
       int top = 31 - __clz(gmin ^ gmax);  // highest bit where candidates differ
       kprefix = (uint32_t)((uint64_t)gmax >> (top + 1));  // shared by every key
-      while (true) {
+      for (int pass = 0;; ++pass) {
+        uint32_t* h = hist[pass & 1];
+        uint32_t* h_next = hist[(pass + 1) & 1];
         const int width = min(kDigitBits, top + 1);
         shift = top + 1 - width;
-        for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
-        __syncthreads();
-#pragma unroll 8
         for (int j = 0; j < cols; ++j) {
           const int i = tid + kSelThreads * j;
           const uint32_t key = skey[i];
           if (i < C && (uint32_t)((uint64_t)key >> (shift + width)) == kprefix)
-            atomicAdd(&hist[(key >> shift) & ((1u << width) - 1u)], 1u);
+            atomicAdd(&h[(key >> shift) & ((1u << width) - 1u)], 1u);
         }
+        for (int i = tid; i < kBins; i += kSelThreads) h_next[i] = 0;  // for the next pass
         __syncthreads();
         if (wave == 0) {
           // lane l owns digits 2047 - 32 l ... 2016 - 32 l (largest first)
           constexpr int PER_LANE = kBins / kWave;
           uint32_t s = 0;
 #pragma unroll
-          for (int j = 0; j < PER_LANE; ++j) s += hist[kBins - 1 - PER_LANE * lane - j];
-          uint32_t incl = s;
-#pragma unroll
-          for (int off = 1; off < kWave; off <<= 1) {
-            const uint32_t y = __shfl_up(incl, off);
-            if (lane >= off) incl += y;
-          }
+          for (int j = 0; j < PER_LANE; ++j) s += h[kBins - 1 - PER_LANE * lane - j];
+          const uint32_t incl = wave_incl_sum(s);
           const int f = __ffsll((long long)__ballot(incl >= need)) - 1;  // first lane reaching `need`
-          const uint32_t before = __shfl(incl - s, f);                   // keys in larger digits
-          // the whole wave scans lane f's 32 digits
+          const uint32_t before = (uint32_t)__builtin_amdgcn_readlane((int)(incl - s), f);
+          // the wave scans lane f's 32 digits (lanes 32..63 carry zeros)
           const uint32_t digit = (uint32_t)(kBins - 1 - PER_LANE * f - (lane & (PER_LANE - 1)));
-          const uint32_t c = (lane < PER_LANE) ? hist[digit] : 0u;
-          uint32_t ic = c;
-#pragma unroll
-          for (int off = 1; off < PER_LANE; off <<= 1) {
-            const uint32_t y = __shfl_up(ic, off);
-            if (lane >= off) ic += y;
-          }
+          const uint32_t c = (lane < PER_LANE) ? h[digit] : 0u;
+          const uint32_t ic = wave_incl_sum(c);
           const unsigned long long hit = __ballot(lane < PER_LANE && before + ic >= need);
           if (lane == __ffsll((long long)hit) - 1) {
             const uint32_t cum = before + ic - c;
@@ -156,111 +170,63 @@ __global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
         __syncthreads();
         kprefix = s_prefix;
         need = s_need;
-        const bool done = s_done;
-        __syncthreads();
-        if (done || shift == 0) break;
+        if (s_done || shift == 0) break;
         top = shift - 1;
       }
     }
   }
 
-  // ---- 3. ranks in page-id order: id = tid + 1024 j, i.e. ordered by (j, wave, lane)
-  const unsigned long long below = lanes_below();
-  if (radix) {
-#pragma unroll 8
-    for (int j = 0; j < cols; ++j) {
-      {
-        const bool v = tid + kSelThreads * j < C;
-        const uint32_t kt = skey[tid + kSelThreads * j] >> shift;
-        const unsigned long long ga = __ballot(v && kt > kprefix);
-        const unsigned long long ge = __ballot(v && kt == kprefix);
-        if (lane == 0) {
-          cnt_a[j][wave] = popc64(ga);
-          cnt_e[j][wave] = popc64(ge);
-        }
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // exclusive prefixes over the (column, wave) order, 64 slots per pass:
-      // tie-rank base first, then the output slot base
-      int e_run = 0, o_run = 0;
-      for (int s0 = 0; s0 < cols * kSelWaves; s0 += kWave) {
-        const int sidx = s0 + lane;
-        const bool in = sidx < cols * kSelWaves;
-        const int jj = in ? sidx / kSelWaves : 0, ww = in ? sidx % kSelWaves : 0;
-        const int ce = in ? cnt_e[jj][ww] : 0, ca = in ? cnt_a[jj][ww] : 0;
-        int ie = ce;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-          const int y = __shfl_up(ie, off);
-          if (lane >= off) ie += y;
-        }
-        const int ebase = e_run + ie - ce;
-        const int taken = ca + max(0, min((int)need - ebase, ce));
-        int io = taken;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-          const int y = __shfl_up(io, off);
-          if (lane >= off) io += y;
-        }
-        if (in) {
-          cnt_e[jj][ww] = ebase;
-          cnt_a[jj][ww] = o_run + io - taken;
-        }
-        e_run += __shfl(ie, kWave - 1);
-        o_run += __shfl(io, kWave - 1);
-      }
-    }
-    __syncthreads();
-  }
-
+  // ---- 3. per-wave ballots of "above the threshold" and "tied with it" are
+  // 64-bit words of id-ordered bitmaps (candidate i = tid + 1024 j is bit lane
+  // of word 16 j + wave); page-table entries replace the keys in LDS.
   const int n_pre = (Pe + kPage - 1) / kPage;
   const int w0 = max(Ws, Pe);
   const int n_win = (L > w0) ? (L + kPage - 1) / kPage - w0 / kPage : 0;
   const int n_items = n_pre + k + n_win;
   int32_t* wrk = work ? work + 4 * (size_t)unit * max_items : nullptr;
   int32_t* sel = sel_pages ? sel_pages + (size_t)unit * budget : nullptr;
-
-  // ---- 4. selected pages: output slot = base of (column, wave) + taken lanes below
-  auto emit = [&](int o, int i, int phys) {
+  auto emit = [&](int o, int i, int ph) {
     const int p = c_lo + i;
     if (sel) sel[o] = p;
     if (wrk)
-      put_item(wrk, n_pre + o, p, phys, max(p * kPage, Pe) - p * kPage,
-               min(p * kPage + kPage, Ws) - p * kPage);
+      put_item(wrk, n_pre + o, p, ph, max(p * kPage, Pe) - p * kPage, min(p * kPage + kPage, Ws) - p * kPage);
   };
   if (take_all) {
-#pragma unroll 4
     for (int j = 0; j < cols; ++j) {
       const int i = tid + kSelThreads * j;
-      const int phys = pt[c_lo + min(i, C - 1)];
-      if (i < C) emit(i, i, phys);
+      const int ph = ptc[min(i, C - 1)];
+      if (i < C) emit(i, i, ph);
     }
   } else if (radix) {
-    uint32_t mine = 0;  // columns where this lane's page is taken
-#pragma unroll 8
-    for (int j = 0; j < cols; ++j) {
-      {
+#pragma unroll
+    for (int j = 0; j < kCols; ++j) {
+      if (j < cols) {
         const int i = tid + kSelThreads * j;
-        const bool v = i < C;
         const uint32_t kt = skey[i] >> shift;
-        const bool a = v && kt > kprefix, e = v && kt == kprefix;
-        const unsigned long long ge = __ballot(e);
-        const int rank = cnt_e[j][wave] + popc64(ge & below);
-        const bool take = a || (e && rank < (int)need);
-        const unsigned long long gt = __ballot(take);
-        if (take) {
-          mine |= 1u << j;
-          skey[i] = (uint32_t)(cnt_a[j][wave] + popc64(gt & below));  // reuse: output slot
+        const bool v = i < C;
+        const unsigned long long ga = __ballot(v && kt > kprefix);
+        const unsigned long long ge = __ballot(v && kt == kprefix);
+        if (lane == 0) {
+          bm_gt[j * kSelWaves + wave] = ga;
+          bm_eq[j * kSelWaves + wave] = ge;
         }
+        skey[i] = (uint32_t)phys[j];
       }
     }
-    while (mine) {
-      const int j = __ffs(mine) - 1;
-      mine &= mine - 1;
-      const int i = tid + kSelThreads * j;
-      emit((int)skey[i], i, pt[c_lo + i]);
+    __syncthreads();
+    // tied keys are taken in id order up to `need`; then output slots in id order
+    const int nwords = cols * kSelWaves;  // <= 1024 = one word per thread
+    const unsigned long long eqw = tid < nwords ? bm_eq[tid] : 0ull;
+    const int ebase = block_excl_sum(popc64(eqw), scan_sh);
+    unsigned long long takew = tid < nwords ? bm_gt[tid] : 0ull;
+    int left = (int)need - ebase;  // ties of this word still to take
+    for (unsigned long long m = eqw; m && left > 0; m &= m - 1, --left) takew |= m & (~m + 1);
+    int o = block_excl_sum(popc64(takew), scan_sh);
+    const int jw = tid / kSelWaves, ww = tid % kSelWaves;  // word tid covers ids 1024 jw + 64 ww + bit
+    for (unsigned long long m = takew; m; m &= m - 1) {
+      const int bit = __ffsll((long long)m) - 1;
+      const int i = kSelThreads * jw + kWave * ww + bit;
+      emit(o++, i, (int)skey[i]);
     }
   }
 

@@ -16,11 +16,12 @@
  *
  * Conventions for every entry point
  *   - Pointers marked "device" point to GPU memory; the caller allocates and
- *     owns every buffer (the library allocates nothing and keeps no state
- *     besides a thread-local error message).
+ *     owns every buffer.  The library allocates nothing; its only state is a
+ *     thread-local error message and device properties (CU count, kernel
+ *     occupancy) cached on first use.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
- *     returns without synchronising.  Nothing is captured-unsafe: no
- *     allocation, no memset, no host synchronisation.
+ *     returns without synchronising: no allocation, no memset, no host
+ *     synchronisation, so calls can be captured into a HIP graph.
  *   - Host-detectable argument errors return a non-zero fsa_status before any
  *     launch; fsa_last_error() then describes it.  A failed launch returns
  *     FSA_ERR_HIP.  Device-resident data (page tables, lengths) is trusted.
