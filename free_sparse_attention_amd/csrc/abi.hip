@@ -91,9 +91,9 @@ int max_items_of(const fsa_dims* d, fsa_layer_cfg c, int32_t max_seq_len) {
   return (int)std::max<long>(1, pre + sel + win);
 }
 
-// Workspace of the sparse step: [scores][work][counts][part_ml][part_o]
+// Workspace of the sparse step: [scores][work][part_ml][part_o]
 struct SparseWs {
-  size_t scores, work, counts, part_ml, part_o, total;
+  size_t scores, work, part_ml, part_o, total;
   int max_items;
   fsa::AttnPlan plan;
 };
@@ -107,7 +107,6 @@ SparseWs sparse_ws(const fsa_dims* d, fsa_layer_cfg c, int32_t max_seq_len) {
   size_t o = 0;
   w.scores = o;   o = align256(o + units * d->max_pages_per_seq * sizeof(float));
   w.work = o;     o = align256(o + units * w.max_items * 4 * sizeof(int32_t));
-  w.counts = o;   o = align256(o + units * 2 * sizeof(int32_t));
   w.part_ml = o;  o = align256(o + units * w.plan.wg_per_unit * G * 2 * sizeof(float));
   w.part_o = o;   o = align256(o + units * w.plan.wg_per_unit * G * d->head_dim * sizeof(float));
   w.total = o;
@@ -136,7 +135,7 @@ DenseWs dense_ws(const fsa_dims* d, int32_t max_seq_len) {
 fsa::AttnArgs attn_args(const fsa_dims* dims, int max_items, float sm_scale, int32_t max_seq_len,
                         const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* page_table, const int32_t* seq_lens, const int32_t* work,
-                        const int32_t* counts, float* part_o, float* part_ml, void* out) {
+                        float* part_o, float* part_ml, void* out) {
   fsa::AttnArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.kc = static_cast<const uint16_t*>(k_cache);
@@ -144,7 +143,6 @@ fsa::AttnArgs attn_args(const fsa_dims* dims, int max_items, float sm_scale, int
   a.page_table = page_table;
   a.seq_lens = seq_lens;
   a.work = work;
-  a.counts = counts;
   a.part_o = part_o;
   a.part_ml = part_ml;
   a.out = static_cast<uint16_t*>(out);
@@ -307,14 +305,13 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
       "quest_scores launch"));
   FSA_CHECK(hip_status(
       fsa::launch_select_pages(at<float>(workspace, w.scores), page_table, seq_lens, sel_pages,
-                               at<int32_t>(workspace, w.work), at<int32_t>(workspace, w.counts),
-                               dims->batch, dims->num_kv_heads, dims->max_pages_per_seq,
+                               at<int32_t>(workspace, w.work), nullptr, dims->batch, dims->num_kv_heads, dims->max_pages_per_seq,
                                cfg.prefix_tokens, cfg.window_tokens, cfg.budget_pages, w.max_items,
                                max_seq_len, st),
       "select_pages launch"));
   const fsa::AttnArgs a = attn_args(dims, w.max_items, sm_scale, max_seq_len, q, k_cache, v_cache,
                                     page_table, seq_lens, at<int32_t>(workspace, w.work),
-                                    at<int32_t>(workspace, w.counts), at<float>(workspace, w.part_o),
+                                    at<float>(workspace, w.part_o),
                                     at<float>(workspace, w.part_ml), out);
   return hip_status(fsa::launch_attention(fsa::kList, w.plan, a, st), "decode attention launch");
 }
@@ -341,7 +338,7 @@ fsa_status fsa_dense_decode_attn(const fsa_dims* dims, float sm_scale, int32_t m
   if (!workspace || workspace_bytes < w.total)
     return fail(FSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, w.total);
   const fsa::AttnArgs a = attn_args(dims, w.max_items, sm_scale, max_seq_len, q, k_cache, v_cache,
-                                    page_table, seq_lens, nullptr, nullptr, at<float>(workspace, w.part_o),
+                                    page_table, seq_lens, nullptr, at<float>(workspace, w.part_o),
                                     at<float>(workspace, w.part_ml), out);
   return hip_status(fsa::launch_attention(fsa::kDense, w.plan, a, static_cast<hipStream_t>(stream)),
                     "dense decode attention launch");

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256, 3) void decode_attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ work,
-    const int32_t* __restrict__ counts, float* __restrict__ part_o, float* __restrict__ part_ml,
+    float* __restrict__ part_o, float* __restrict__ part_ml,
     uint16_t* __restrict__ out, int hq, int hkv, int max_pages, int max_items, int ipw,
     int wg_per_unit, float scale_log2, int max_seq_len) {
   constexpr int NKS = D / 32;  // QK k-steps
@@ -50,28 +50,34 @@ __global__ __launch_bounds__(256, 3) void decode_attention_kernel(
   const int b = unit / hkv, g = unit % hkv, G = hq / hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, gq = lane >> 4;
-  const int L = min(seq_lens[b], max_seq_len);  // lengths beyond the host bound are clamped
-  const int n_items = MODE == kDense ? (L + kPage - 1) / kPage : counts[2 * unit + 1];
   const int per_wg = kAttnWaves * ipw;
-  const int n_wg = (n_items + per_wg - 1) / per_wg;
-  if (wg >= n_wg) return;
   const int i_begin = wg * per_wg + wave * ipw;
-  const int n = max(0, min(ipw, n_items - i_begin));
 
-  // item descriptors of this wave: lane j holds item i_begin + j
-  const int32_t* pt = page_table + (size_t)b * max_pages;
-  int my_phys = 0, my_lo = 0, my_hi = 0;
-  if (lane < n) {
-    const int i = i_begin + lane;
-    if (MODE == kDense) {
-      my_phys = pt[i];
+  // item descriptors of this wave: lane j holds item i_begin + j.  Dense items
+  // are the sequence's pages.  A work list is padded with empty items (lo = hi)
+  // to max_items, so its entries are read without first loading the item
+  // count; the valid items of a wave are a prefix of its lanes.
+  int my_phys = 0, my_lo = 0, my_hi = 0, n, n_wg;
+  if (MODE == kDense) {
+    const int L = min(seq_lens[b], max_seq_len);  // lengths beyond the host bound are clamped
+    const int n_items = (L + kPage - 1) / kPage;
+    n_wg = (n_items + per_wg - 1) / per_wg;
+    if (wg >= n_wg) return;
+    n = max(0, min(ipw, n_items - i_begin));
+    if (lane < n) {
+      const int i = i_begin + lane;
+      my_phys = page_table[(size_t)b * max_pages + i];
       my_hi = min(kPage, L - i * kPage);
-    } else {
-      const int4 it = *reinterpret_cast<const int4*>(work + 4 * ((size_t)unit * max_items + i));
+    }
+  } else {
+    n_wg = wg_per_unit;
+    if (lane < ipw && i_begin + lane < max_items) {
+      const int4 it = *reinterpret_cast<const int4*>(work + 4 * ((size_t)unit * max_items + i_begin + lane));
       my_phys = it.y;
       my_lo = it.z;
       my_hi = it.w;
     }
+    n = __popcll(__ballot(my_lo < my_hi));
   }
 
   // B operand of QK: q[head col][32 ks + 8 gq .. +8] (zero rows beyond G)
@@ -184,12 +190,13 @@ __global__ __launch_bounds__(256, 3) void decode_attention_kernel(
     float o = 0.f, l = 0.f;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) {
-      const float e = exp2f(sh_m[w][h] - M);  // waves without items carry m = -inf
+      const float mw = sh_m[w][h];
+      const float e = mw == -INFINITY ? 0.f : exp2f(mw - M);  // waves without items carry m = -inf
       o += e * sh_o[w][d][h];
       l += e * sh_l[w][h];
     }
     if (direct) {
-      out[((size_t)b * hq + (size_t)g * G + h) * D + d] = (uint16_t)f32_to_bf16_bits(o / l);
+      out[((size_t)b * hq + (size_t)g * G + h) * D + d] = (uint16_t)f32_to_bf16_bits(l > 0.f ? o / l : 0.f);
     } else {
       po[idx] = o;
       if (d == 0) {
@@ -208,8 +215,7 @@ __global__ __launch_bounds__(256, 3) void decode_attention_kernel(
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ counts,
-    uint16_t* __restrict__ out, int hq, int hkv, int per_wg, int wg_per_unit, int max_seq_len) {
+    const int32_t* __restrict__ seq_lens, uint16_t* __restrict__ out, int hq, int hkv, int per_wg, int wg_per_unit, int max_seq_len) {
   constexpr int NQ = D / 4;            // float4 columns of one head
   constexpr int PARTS = 256 / NQ;      // threads summing disjoint subsets of partials
   __shared__ float sh_e[kMaxPartials];
@@ -217,9 +223,13 @@ __global__ __launch_bounds__(256) void combine_kernel(
   const int G = hq / hkv;
   const int unit = blockIdx.x / G, h = blockIdx.x % G;
   const int b = unit / hkv, g = unit % hkv;
-  const int L = min(seq_lens[b], max_seq_len);
-  const int n_items = MODE == kDense ? (L + kPage - 1) / kPage : counts[2 * unit + 1];
-  const int n = (n_items + per_wg - 1) / per_wg;
+  // partial slots in use: a work list fills all of them (empty ones carry
+  // m = -inf); dense units use as many as their length needs
+  int n = wg_per_unit;
+  if (MODE == kDense) {
+    const int L = min(seq_lens[b], max_seq_len);
+    n = ((L + kPage - 1) / kPage + per_wg - 1) / per_wg;
+  }
   if (n <= 1) return;  // written directly by the attention kernel
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* ml = part_ml + 2 * (size_t)unit * wg_per_unit * G;
@@ -230,7 +240,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float l_loc = 0.f;
   for (int w = lane; w < n; w += kWave) {
-    const float e = exp2f(ml[2 * ((size_t)w * G + h)] - M);
+    const float mw = ml[2 * ((size_t)w * G + h)];
+    const float e = mw == -INFINITY ? 0.f : exp2f(mw - M);
     if (wave == 0) sh_e[w] = e;
     l_loc += e * ml[2 * ((size_t)w * G + h) + 1];
   }
@@ -262,7 +273,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
       a.z += v.z;
       a.w += v.w;
     }
-    const float inv = 1.0f / Lsum;
+    const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
     const uint32_t w0 = f32_to_bf16_bits(a.x * inv) | (f32_to_bf16_bits(a.y * inv) << 16);
     const uint32_t w1 = f32_to_bf16_bits(a.z * inv) | (f32_to_bf16_bits(a.w * inv) << 16);
     *reinterpret_cast<uint2*>(out + ((size_t)b * hq + (size_t)g * G + h) * D + 4 * c4) = make_uint2(w0, w1);
@@ -295,12 +306,12 @@ hipError_t launch_attention(AttnMode mode, const AttnPlan& plan, const AttnArgs&
 #define FSA_ATTN(DD, MM)                                                                              \
   do {                                                                                                \
     hipLaunchKernelGGL((decode_attention_kernel<DD, MM>), grid, dim3(256), 0, stream, a.q, a.kc, a.vc,  \
-                       a.page_table, a.seq_lens, a.work, a.counts, a.part_o, a.part_ml, a.out, a.hq,   \
+                       a.page_table, a.seq_lens, a.work, a.part_o, a.part_ml, a.out, a.hq,   \
                        a.hkv, a.max_pages, a.max_items, plan.items_per_wave, plan.wg_per_unit,        \
                        a.scale_log2, a.max_seq_len);                                                   \
     if (plan.wg_per_unit > 1)                                                                         \
       hipLaunchKernelGGL((combine_kernel<DD, MM>), dim3((unsigned)(a.batch * a.hq)), dim3(256), 0,     \
-                         stream, a.part_o, a.part_ml, a.seq_lens, a.counts, a.out, a.hq, a.hkv,        \
+                         stream, a.part_o, a.part_ml, a.seq_lens, a.out, a.hq, a.hkv,        \
                          kAttnWaves * plan.items_per_wave, plan.wg_per_unit, a.max_seq_len);           \
   } while (0)
   if (a.d == 128) {

@@ -152,7 +152,6 @@ struct AttnArgs {
   const int32_t* page_table;
   const int32_t* seq_lens;
   const int32_t* work;    // selection work items (kList)
-  const int32_t* counts;  // (k, items) per unit (kList)
   float* part_o;
   float* part_ml;
   uint16_t* out;

@@ -3,11 +3,14 @@
 // The paper (Abstract; analysis page "Methodology"; digest "The Move") keeps
 // a fixed budget of query-aware top-k pages next to the prefix and the
 // window.  Here, per (sequence, KV head), one workgroup of 1024 threads:
-//   1. loads the candidates' scores as order-preserving 32-bit keys into LDS
-//      (128 KiB: up to 32768 candidates) and their page-table entries into
-//      registers; thread t handles candidates t, t + 1024, ... so every load
-//      instruction reads 256 contiguous bytes and LDS accesses are
-//      bank-conflict free;
+//   1. loads the scores of logical pages [0, n_max) as order-preserving
+//      32-bit keys into LDS (128 KiB: up to 32768 pages) and their page-table
+//      entries into registers; n_max comes from the host-side length bound,
+//      so these loads are issued together with the load of the sequence
+//      length instead of after it.  Thread t handles pages t, t + 1024, ...
+//      so every load instruction reads 256 contiguous bytes and LDS accesses
+//      are bank-conflict free.  Only candidates -- the pages that meet the
+//      middle region [Pe, Ws) -- take part in what follows;
 //   2. finds the k-th largest key exactly by most-significant-digit radix
 //      select.  Digits start right below the bits that the smallest and the
 //      largest key share, 11 bits at a time (2048 LDS bins, double-buffered
@@ -16,13 +19,15 @@
 //      and the search stops as soon as that digit's bin holds exactly the
 //      number of keys still needed;
 //   3. turns per-wave ballots ("above the threshold", "tied with it") into
-//      id-ordered bitmaps; block-wide prefix sums of their popcounts take the
-//      tied pages in id order (ties go to the lower page id) and give every
-//      selected page its output slot, so pages come out ascending;
+//      page-ordered bitmaps; block-wide prefix sums of their popcounts take
+//      the tied pages in page order (ties go to the lower page id) and give
+//      every selected page its output slot, so pages come out ascending;
 //   4. writes the attended tokens as work items.  The attended set is split
 //      into three disjoint token ranges -- prefix [0, Pe), the middle tokens
 //      [Pe, Ws) of selected pages and the window [max(Ws, Pe), L) -- so no
-//      token appears twice and no sort or dedup pass is needed.
+//      token appears twice and no sort or dedup pass is needed.  The list is
+//      padded with empty items up to its fixed length, so a consumer can
+//      start on it without first reading how many items it holds.
 // Wave-level scans and reductions use DPP row operations.
 #include "fsa_internal.h"
 
@@ -31,8 +36,8 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kCols = 32;  // candidates per thread: up to 32768 (512k tokens)
-constexpr int kMaxCand = kSelThreads * kCols;
+constexpr int kCols = 32;  // pages per thread: up to 32768 (512k tokens)
+constexpr int kMaxPagesSel = kSelThreads * kCols;
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
 
@@ -60,61 +65,60 @@ __global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
     const int32_t* __restrict__ seq_lens, int32_t* __restrict__ sel_pages,
     int32_t* __restrict__ work, int32_t* __restrict__ counts, int hkv, int max_pages, int prefix,
     int window, int budget, int max_items, int max_seq_len) {
-  __shared__ uint32_t skey[kMaxCand];
+  __shared__ uint32_t skey[kMaxPagesSel];
   __shared__ uint32_t hist[2][kBins];
-  __shared__ unsigned long long bm_gt[kCols * kSelWaves];  // id-ordered bitmap: key above the threshold
-  __shared__ unsigned long long bm_eq[kCols * kSelWaves];  // id-ordered bitmap: key tied with it
+  __shared__ unsigned long long bm_gt[kCols * kSelWaves];  // page-ordered bitmap: key above the threshold
+  __shared__ unsigned long long bm_eq[kCols * kSelWaves];  // page-ordered bitmap: key tied with it
   __shared__ int scan_sh[kSelWaves + 1];
   __shared__ uint32_t mm_sh[2 * kSelWaves];
   __shared__ uint32_t s_prefix, s_need, s_done;
 
   const int unit = blockIdx.x, b = unit / hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_max = (max_seq_len + kPage - 1) / kPage;         // pages any sequence can have
+  const int cols = (n_max + kSelThreads - 1) / kSelThreads;  // uniform
+  const float* sc = scores + (size_t)unit * max_pages;
+  const int32_t* pt = page_table + (size_t)b * max_pages;
+
+  // ---- 1. scores and page-table entries of pages tid + 1024 j, loaded
+  // together with the sequence length
+  int phys[kCols];
+  uint32_t raw[kCols];
+#pragma unroll
+  for (int j = 0; j < kCols; ++j) {
+    if (j < cols) {
+      const int p = min(tid + kSelThreads * j, n_max - 1);
+      raw[j] = __float_as_uint(sc[p]);
+      phys[j] = pt[p];
+    }
+  }
   const int L = min(seq_lens[b], max_seq_len);  // lengths beyond the host bound are clamped
   const int Pe = min(prefix, L), Ws = max(0, L - window);
   const int c_lo = Pe / kPage;
-  const int C = (Pe < Ws) ? (Ws + kPage - 1) / kPage - c_lo : 0;
+  const int c_hi = (Pe < Ws) ? (Ws + kPage - 1) / kPage : c_lo;  // candidates: pages [c_lo, c_hi)
+  const int C = c_hi - c_lo;
   const int k = min(budget, C);
-  const bool take_all = (k == C);
-  const bool radix = !take_all && k > 0;
-  const int cols = (C + kSelThreads - 1) / kSelThreads;  // uniform
-  const float* sc = scores + (size_t)unit * max_pages + c_lo;
-  const int32_t* pt = page_table + (size_t)b * max_pages;
-  const int32_t* ptc = pt + c_lo;
-
-  // ---- 1. keys (LDS) and page-table entries (registers) of candidates tid + 1024 j;
-  // every load is issued before the first one is used
-  int phys[kCols];
-  uint32_t raw[kCols];
+  const bool radix = k > 0 && k < C;  // otherwise every candidate is taken (k = C) or none is
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  if (radix) {
 #pragma unroll
-    for (int j = 0; j < kCols; ++j) {
-      if (j < cols) {
-        const int ic = min(tid + kSelThreads * j, C - 1);
-        raw[j] = __float_as_uint(sc[ic]);
-        phys[j] = ptc[ic];
+  for (int j = 0; j < kCols; ++j) {
+    if (j < cols) {
+      const int p = tid + kSelThreads * j;
+      const uint32_t key = f32_order_key(__uint_as_float(raw[j]));  // non-candidates: never used
+      skey[p] = key;
+      if (p >= c_lo && p < c_hi) {
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
       }
     }
-#pragma unroll
-    for (int j = 0; j < kCols; ++j) {
-      if (j < cols) {
-        const int i = tid + kSelThreads * j;
-        const uint32_t key = f32_order_key(__uint_as_float(raw[j]));
-        skey[i] = key;
-        if (i < C) {
-          kmin = min(kmin, key);
-          kmax = max(kmax, key);
-        }
-      }
-    }
-    for (int i = tid; i < kBins; i += kSelThreads) hist[0][i] = 0;
   }
+  for (int i = tid; i < kBins; i += kSelThreads) hist[0][i] = 0;
 
   // ---- 2. exact k-th largest key: keys >> shift compared with kprefix, `need` ties to take
-  uint32_t kprefix = 0, need = (uint32_t)k;
+  uint32_t kprefix = 0, need = 0;
   int shift = 0;
   if (radix) {
+    need = (uint32_t)k;
     kmin = wave_min(kmin);
     kmax = wave_max(kmax);
     if (lane == 0) {
@@ -139,9 +143,9 @@ __global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
         const int width = min(kDigitBits, top + 1);
         shift = top + 1 - width;
         for (int j = 0; j < cols; ++j) {
-          const int i = tid + kSelThreads * j;
-          const uint32_t key = skey[i];
-          if (i < C && (uint32_t)((uint64_t)key >> (shift + width)) == kprefix)
+          const int p = tid + kSelThreads * j;
+          const uint32_t key = skey[p];
+          if (p >= c_lo && p < c_hi && (uint32_t)((uint64_t)key >> (shift + width)) == kprefix)
             atomicAdd(&h[(key >> shift) & ((1u << width) - 1u)], 1u);
         }
         for (int i = tid; i < kBins; i += kSelThreads) h_next[i] = 0;  // for the next pass
@@ -176,69 +180,60 @@ __global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
     }
   }
 
-  // ---- 3. per-wave ballots of "above the threshold" and "tied with it" are
-  // 64-bit words of id-ordered bitmaps (candidate i = tid + 1024 j is bit lane
-  // of word 16 j + wave); page-table entries replace the keys in LDS.
+  // ---- 3. page-ordered bitmaps: page tid + 1024 j is bit `lane` of word
+  // 16 j + wave; page-table entries replace the keys in LDS
+  const bool take_all = k == C;
+#pragma unroll
+  for (int j = 0; j < kCols; ++j) {
+    if (j < cols) {
+      const int p = tid + kSelThreads * j;
+      const bool cand = p >= c_lo && p < c_hi;
+      const uint32_t kt = skey[p] >> shift;
+      const unsigned long long ga = __ballot(cand && (radix ? kt > kprefix : take_all));
+      const unsigned long long ge = __ballot(cand && radix && kt == kprefix);
+      if (lane == 0) {
+        bm_gt[j * kSelWaves + wave] = ga;
+        bm_eq[j * kSelWaves + wave] = ge;
+      }
+      skey[p] = (uint32_t)phys[j];
+    }
+  }
+  __syncthreads();
+  // tied pages are taken in page order up to `need`; then output slots in page order
+  const int nwords = cols * kSelWaves;  // <= 512: at most one word per thread
+  const unsigned long long eqw = tid < nwords ? bm_eq[tid] : 0ull;
+  const int ebase = block_excl_sum(popc64(eqw), scan_sh);
+  unsigned long long takew = tid < nwords ? bm_gt[tid] : 0ull;
+  int left = (int)need - ebase;  // ties of this word still to take
+  for (unsigned long long m = eqw; m && left > 0; m &= m - 1, --left) takew |= m & (~m + 1);
+  int o = block_excl_sum(popc64(takew), scan_sh);
+
+  // ---- 4. work items: prefix [0, n_pre), selected [n_pre, n_pre + k), window,
+  // then empty items up to max_items
   const int n_pre = (Pe + kPage - 1) / kPage;
   const int w0 = max(Ws, Pe);
   const int n_win = (L > w0) ? (L + kPage - 1) / kPage - w0 / kPage : 0;
   const int n_items = n_pre + k + n_win;
   int32_t* wrk = work ? work + 4 * (size_t)unit * max_items : nullptr;
   int32_t* sel = sel_pages ? sel_pages + (size_t)unit * budget : nullptr;
-  auto emit = [&](int o, int i, int ph) {
-    const int p = c_lo + i;
+  const int jw = tid / kSelWaves, ww = tid % kSelWaves;  // word tid covers pages 1024 jw + 64 ww + bit
+  for (unsigned long long m = takew; m; m &= m - 1) {
+    const int p = kSelThreads * jw + kWave * ww + (__ffsll((long long)m) - 1);
     if (sel) sel[o] = p;
     if (wrk)
-      put_item(wrk, n_pre + o, p, ph, max(p * kPage, Pe) - p * kPage, min(p * kPage + kPage, Ws) - p * kPage);
-  };
-  if (take_all) {
-    for (int j = 0; j < cols; ++j) {
-      const int i = tid + kSelThreads * j;
-      const int ph = ptc[min(i, C - 1)];
-      if (i < C) emit(i, i, ph);
-    }
-  } else if (radix) {
-#pragma unroll
-    for (int j = 0; j < kCols; ++j) {
-      if (j < cols) {
-        const int i = tid + kSelThreads * j;
-        const uint32_t kt = skey[i] >> shift;
-        const bool v = i < C;
-        const unsigned long long ga = __ballot(v && kt > kprefix);
-        const unsigned long long ge = __ballot(v && kt == kprefix);
-        if (lane == 0) {
-          bm_gt[j * kSelWaves + wave] = ga;
-          bm_eq[j * kSelWaves + wave] = ge;
-        }
-        skey[i] = (uint32_t)phys[j];
-      }
-    }
-    __syncthreads();
-    // tied keys are taken in id order up to `need`; then output slots in id order
-    const int nwords = cols * kSelWaves;  // <= 1024 = one word per thread
-    const unsigned long long eqw = tid < nwords ? bm_eq[tid] : 0ull;
-    const int ebase = block_excl_sum(popc64(eqw), scan_sh);
-    unsigned long long takew = tid < nwords ? bm_gt[tid] : 0ull;
-    int left = (int)need - ebase;  // ties of this word still to take
-    for (unsigned long long m = eqw; m && left > 0; m &= m - 1, --left) takew |= m & (~m + 1);
-    int o = block_excl_sum(popc64(takew), scan_sh);
-    const int jw = tid / kSelWaves, ww = tid % kSelWaves;  // word tid covers ids 1024 jw + 64 ww + bit
-    for (unsigned long long m = takew; m; m &= m - 1) {
-      const int bit = __ffsll((long long)m) - 1;
-      const int i = kSelThreads * jw + kWave * ww + bit;
-      emit(o++, i, (int)skey[i]);
-    }
+      put_item(wrk, n_pre + o, p, (int)skey[p], max(p * kPage, Pe) - p * kPage,
+               min(p * kPage + kPage, Ws) - p * kPage);
+    ++o;
   }
-
-  // ---- 5. prefix and window items, padding, counts
   if (wrk) {
     for (int i = tid; i < n_pre; i += kSelThreads)
-      put_item(wrk, i, i, pt[i], 0, min(kPage, Pe - i * kPage));
+      put_item(wrk, i, i, (int)skey[i], 0, min(kPage, Pe - i * kPage));
     for (int i = tid; i < n_win; i += kSelThreads) {
       const int p = w0 / kPage + i;
-      put_item(wrk, n_pre + k + i, p, pt[p], max(p * kPage, w0) - p * kPage,
+      put_item(wrk, n_pre + k + i, p, (int)skey[p], max(p * kPage, w0) - p * kPage,
                min(p * kPage + kPage, L) - p * kPage);
     }
+    for (int i = n_items + tid; i < max_items; i += kSelThreads) put_item(wrk, i, -1, 0, 0, 0);
   }
   if (sel)
     for (int i = k + tid; i < budget; i += kSelThreads) sel[i] = -1;
@@ -250,7 +245,7 @@ __global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
 
 }  // namespace
 
-int select_max_candidates() { return kMaxCand; }
+int select_max_candidates() { return kMaxPagesSel; }
 
 hipError_t launch_select_pages(const float* scores, const int32_t* page_table,
                                const int32_t* seq_lens, int32_t* sel_pages, int32_t* work,

@@ -146,8 +146,12 @@ int32_t fsa_max_work_items(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_
  *   work       int32 [B][Hkv][max_items][4] (device) or NULL, max_items =
  *              fsa_max_work_items(): the attended tokens as (logical page,
  *              pool page, first slot, end slot) items in ascending token
- *              order; every attended token appears in exactly one item
- *   counts     int32 [B][Hkv][2] (device) or NULL: (k, number of items) */
+ *              order; every attended token appears in exactly one item, and
+ *              every such item is non-empty.  Entries after the last item
+ *              are empty items (-1, 0, 0, 0), so the whole array is defined.
+ *   counts     int32 [B][Hkv][2] (device) or NULL: (k, number of items)
+ * Scores of non-candidate pages below ceil(max_seq_len / S) are read but not
+ * used, so they need not be initialised. */
 fsa_status fsa_select_pages(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len,
                             const float* scores, const int32_t* page_table, const int32_t* seq_lens,
                             int32_t* sel_pages, int32_t* work, int32_t* counts, void* stream);

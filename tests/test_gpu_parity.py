@@ -133,7 +133,10 @@ def run_and_check(wl, cfg=None, units=None, q=None, check_scores=True, dense=Tru
         k_gpu = int(counts[b, g, 0])
         assert k_gpu == min(cfg[2], len(cand))
         gsel = [int(p) for p in sel[b, g][:k_gpu]] if cfg[2] > 0 else []
-        mask_gpu = items_to_tokens(work[b, g], int(counts[b, g, 1]), L, wl.page_table[b])
+        n_it = int(counts[b, g, 1])
+        mask_gpu = items_to_tokens(work[b, g], n_it, L, wl.page_table[b])
+        pad = work[b, g, n_it:]
+        assert np.all(pad[:, 2] == pad[:, 3]), f"work-list padding not empty {(b, g)}"
         mask_ora = oracle.attended_mask(L, cfg[0], cfg[1], S, gsel)
         assert np.array_equal(mask_gpu, mask_ora), f"attended set {(b, g)}"
         ref = oracle.attend(qf, K, V, mask_ora, wl.sm_scale)
