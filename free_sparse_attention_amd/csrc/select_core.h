@@ -1,0 +1,302 @@
+// Exact top-k page selection of one (sequence, KV head) by a 1024-thread
+// workgroup, and the merge of the selection with the pinned prefix and the
+// sliding window into a work list.  Used by the stand-alone selection kernel
+// and by the fused scoring + selection kernel.
+//
+// The paper (Abstract; analysis page "Methodology"; digest "The Move") keeps
+// a fixed budget of query-aware top-k pages next to the prefix and the
+// window.  Steps:
+//   1. thread t owns logical pages t, t + 1024, ... below n_max (from the
+//      host-side length bound): it loads their scores and page-table entries
+//      together with the sequence length (one memory round trip) and turns
+//      the scores into order-preserving 32-bit keys kept in registers; the
+//      page-table entries are loaded straight into LDS.  On this CU every instruction of the 1024
+//      threads costs 16 wave issue slots, so each page is touched by as few
+//      instructions as possible;
+//   2. the k-th largest candidate key is found exactly by most-significant-
+//      digit radix select: digits start right below the bits that the
+//      smallest and the largest candidate key share, 11 bits at a time (2048
+//      LDS bins, double-buffered so a pass costs two barriers); one wave scans
+//      the bins for the digit holding the k-th key, and the search stops once
+//      that digit's bin holds exactly the number of keys still needed;
+//   3. per-wave ballots of "taken" form page-ordered 64-bit words (page
+//      t + 1024 j is bit t % 64 of word 16 j + t / 64); every wave scans the
+//      words' popcounts itself, so the output slot of a taken page is a word
+//      prefix plus a popcount within its word: pages come out ascending with
+//      no further barrier.  Only when equal keys straddle the threshold is a
+//      first such scan spent on ranking the tied pages (the lower page id
+//      wins).  Prefix and window items, whose places depend only on the
+//      length and the budget, are written last.
+// The attended set is the disjoint union of three token ranges -- prefix
+// [0, Pe), the middle tokens [Pe, Ws) of selected pages and the window
+// [max(Ws, Pe), L) -- so no token appears twice and no sort or dedup pass is
+// needed.  The list is padded with empty items up to its fixed length.
+#pragma once
+
+#include "fsa_internal.h"
+
+namespace fsa {
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kSelCols = 32;  // pages per thread: up to 32768 (512k tokens)
+constexpr int kSelMaxPages = kSelThreads * kSelCols;
+constexpr int kSelDigitBits = 11;
+constexpr int kSelBins = 1 << kSelDigitBits;
+
+// s_waitcnt immediate for vmcnt(0) with the other counters left alone
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+struct SelectLds {
+  int32_t sphys[kSelMaxPages];  // page-table entries of pages [0, n_max)
+  uint32_t hist[2][kSelBins];
+  __attribute__((aligned(16))) uint32_t cnt[2][kSelCols * kSelWaves];  // per-word popcounts
+  uint32_t mm[2 * kSelWaves];
+  uint32_t s_prefix, s_need, s_done;
+};
+
+// Pages per thread for lengths up to max_seq_len, rounded up to a power of two.
+__host__ __device__ inline int select_cols(int max_seq_len) {
+  const int n = (max_seq_len + kPage - 1) / kPage;
+  int c = 1;
+  while (c * kSelThreads < n) c *= 2;
+  return c;
+}
+
+struct SelectJob {
+  const float* scores;     // the unit's scores, logical page p at [p]
+  const int32_t* pt;       // the sequence's page-table row
+  const int32_t* seq_len;  // the sequence's length (device)
+  const uint32_t* minmax;  // (max key, ~min key) of the candidates, or null: computed here
+  int max_seq_len;
+  int prefix, window, budget, max_items;
+  int32_t* work;    // the unit's work list, or null
+  int32_t* sel;     // the unit's selected pages, or null
+  int32_t* counts;  // the unit's (k, items), or null
+};
+
+__device__ __forceinline__ void put_item(int32_t* work, int idx, int p, int phys, int lo, int hi) {
+  *reinterpret_cast<int4*>(work + 4 * (size_t)idx) = make_int4(p, phys, lo, hi);
+}
+
+// Lanes below this one with their bit set in the wave-uniform mask m.
+__device__ __forceinline__ uint32_t lanes_below(unsigned long long m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Word prefix sums, in page order, of cnt[0 .. nwords) (nwords a multiple of
+// 16).  Returns a per-lane value P such that lane 2 j + wave / 8 of P holds the
+// sum of the words before word 16 j + wave.
+__device__ __forceinline__ uint32_t wave_word_prefix(const uint32_t* cnt, int nwords, int wave, int lane) {
+  uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+  if (8 * lane < nwords) {
+    a = *reinterpret_cast<const uint4*>(cnt + 8 * lane);
+    b = *reinterpret_cast<const uint4*>(cnt + 8 * lane + 4);
+  }
+  const uint32_t c[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  const uint32_t s = (c[0] + c[1]) + (c[2] + c[3]) + ((c[4] + c[5]) + (c[6] + c[7]));
+  uint32_t pre = wave_incl_sum(s) - s;
+  const int r = wave & 7;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) pre += (i < r) ? c[i] : 0u;
+  return pre;
+}
+
+// COLS: pages per thread, a power of two with 1024 COLS >= ceil(max_seq_len / 16)
+// (a compile-time trip count: the per-page loops carry no guards).
+template <int COLS>
+__device__ __forceinline__ void select_unit(SelectLds& S, const SelectJob& J) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_max = (J.max_seq_len + kPage - 1) / kPage;  // pages any sequence can have
+
+  // ---- 1. scores, page-table entries and the length in one round trip
+  // (page-table entries go straight to LDS: sphys[tid + 1024 j])
+  uint32_t key[COLS];
+#pragma unroll
+  for (int j = 0; j < COLS; ++j) {
+    const uint32_t off = 4u * (uint32_t)min(tid + kSelThreads * j, n_max - 1);  // byte offset: base + 32-bit VGPR
+    key[j] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(J.scores) + off);
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(reinterpret_cast<const char*>(J.pt) + off),
+        (__attribute__((address_space(3))) void*)(S.sphys + kSelThreads * j + kWave * wave), 4, 0, 0);
+  }
+  uint32_t mm_in0 = 0, mm_in1 = 0;
+  if (J.minmax) {
+    mm_in0 = J.minmax[0];
+    mm_in1 = J.minmax[1];
+  }
+  const int L = min(*J.seq_len, J.max_seq_len);  // lengths beyond the host bound are clamped
+  const int Pe = min(J.prefix, L), Ws = max(0, L - J.window);
+  const int c_lo = Pe / kPage;
+  const int c_hi = (Pe < Ws) ? (Ws + kPage - 1) / kPage : c_lo;  // candidates: pages [c_lo, c_hi)
+  const int C = c_hi - c_lo;
+  const int k = min(J.budget, C);
+  const bool radix = k > 0 && k < C;  // otherwise every candidate is taken (k = C) or none is
+  const int n_pre = (Pe + kPage - 1) / kPage;
+  const int w0 = max(Ws, Pe);
+  const int w_first = w0 / kPage, n_pages = (L + kPage - 1) / kPage;
+  const int n_win = (L > w0) ? n_pages - w_first : 0;
+  const int n_items = n_pre + k + n_win;
+
+  uint32_t cand = 0;  // bit j: page tid + 1024 j is a candidate
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < COLS; ++j) {
+    const bool c = (uint32_t)(tid + kSelThreads * j - c_lo) < (uint32_t)C;
+    cand |= (uint32_t)c << j;
+    key[j] = f32_order_key(__uint_as_float(key[j]));
+    kmin = c ? min(kmin, key[j]) : kmin;
+    kmax = c ? max(kmax, key[j]) : kmax;
+  }
+
+  // ---- 2. exact k-th largest key: keys >> shift compared with kprefix, `need` ties to take
+  uint32_t kprefix = 0, need = 0;
+  int shift = 0;
+  bool done = false;  // the threshold's bin holds exactly the keys still needed
+  if (radix) {
+    need = (uint32_t)k;
+    for (int i = tid; i < kSelBins; i += kSelThreads) S.hist[0][i] = 0;
+    uint32_t gmin, gmax;
+    if (J.minmax) {
+      gmax = mm_in0;
+      gmin = ~mm_in1;
+      __syncthreads();
+    } else {
+      kmin = wave_min(kmin);
+      kmax = wave_max(kmax);
+      if (lane == 0) {
+        S.mm[2 * wave] = kmin;
+        S.mm[2 * wave + 1] = kmax;
+      }
+      __syncthreads();
+      gmin = wave_min(lane < kSelWaves ? S.mm[2 * lane] : 0xFFFFFFFFu);
+      gmax = wave_max(lane < kSelWaves ? S.mm[2 * lane + 1] : 0u);
+    }
+    if (gmin == gmax) {
+      kprefix = gmin;  // every candidate ties: the lowest ids win
+    } else {
+      int top = 31 - __clz(gmin ^ gmax);                 // highest bit where candidates differ
+      kprefix = (uint32_t)((uint64_t)gmax >> (top + 1));  // shared by every candidate
+      for (int pass = 0;; ++pass) {
+        uint32_t* h = S.hist[pass & 1];
+        uint32_t* h_next = S.hist[(pass + 1) & 1];
+        const int width = min(kSelDigitBits, top + 1);
+        shift = top + 1 - width;
+#pragma unroll
+        for (int j = 0; j < COLS; ++j) {
+          const uint32_t d = key[j] >> shift;  // shift + width <= 32, so d >> width is defined
+          if (((cand >> j) & 1u) && (d >> width) == kprefix) atomicAdd(&h[d & ((1u << width) - 1u)], 1u);
+        }
+        for (int i = tid; i < kSelBins; i += kSelThreads) h_next[i] = 0;  // for the next pass
+        __syncthreads();
+        if (wave == 0) {
+          // lane l owns digits 2047 - 32 l ... 2016 - 32 l (largest first)
+          constexpr int PER_LANE = kSelBins / kWave;
+          const uint4* hv = reinterpret_cast<const uint4*>(h + kSelBins - PER_LANE * (lane + 1));
+          uint32_t part[PER_LANE / 4];
+#pragma unroll
+          for (int v = 0; v < PER_LANE / 4; ++v) {
+            const uint4 x = hv[v];
+            part[v] = (x.x + x.y) + (x.z + x.w);
+          }
+          uint32_t s = 0;
+#pragma unroll
+          for (int v = 0; v < PER_LANE / 4; v += 2) s += part[v] + part[v + 1];
+          const uint32_t incl = wave_incl_sum(s);
+          const int f = __ffsll((long long)__ballot(incl >= need)) - 1;  // first lane reaching `need`
+          const uint32_t before = (uint32_t)__builtin_amdgcn_readlane((int)(incl - s), f);
+          // the wave scans lane f's 32 digits (lanes 32..63 carry zeros)
+          const uint32_t digit = (uint32_t)(kSelBins - 1 - PER_LANE * f - (lane & (PER_LANE - 1)));
+          const uint32_t c = (lane < PER_LANE) ? h[digit] : 0u;
+          const uint32_t ic = wave_incl_sum(c);
+          const unsigned long long hit = __ballot(lane < PER_LANE && before + ic >= need);
+          if (lane == __ffsll((long long)hit) - 1) {
+            const uint32_t cum = before + ic - c;
+            S.s_prefix = (kprefix << width) | digit;
+            S.s_need = need - cum;
+            S.s_done = (c == need - cum);
+          }
+        }
+        __syncthreads();
+        kprefix = S.s_prefix;
+        need = S.s_need;
+        done = S.s_done;
+        if (done || shift == 0) break;
+        top = shift - 1;
+      }
+    }
+  }
+
+  // ---- 3. taken pages -> output slots in page order
+  constexpr int nwords = COLS * kSelWaves;
+  uint32_t tie_take = 0;  // bit j: this lane's tied page of column j is taken
+  if (radix && !done) {
+    // equal keys straddle the threshold: rank the tied pages in page order
+    uint32_t wc = 0;  // lane j: tied pages of column j in this wave
+#pragma unroll
+    for (int j = 0; j < COLS; ++j) {
+      const unsigned long long ge = __ballot(((cand >> j) & 1u) && (key[j] >> shift) == kprefix);
+      wc = lane == j ? (uint32_t)__popcll(ge) : wc;
+    }
+    if (lane < COLS) S.cnt[0][lane * kSelWaves + wave] = wc;
+    __syncthreads();
+    const uint32_t P = wave_word_prefix(S.cnt[0], nwords, wave, lane);
+#pragma unroll
+    for (int j = 0; j < COLS; ++j) {
+      const bool tied = ((cand >> j) & 1u) && (key[j] >> shift) == kprefix;
+      const unsigned long long ge = __ballot(tied);
+      const uint32_t rank = (uint32_t)__builtin_amdgcn_readlane((int)P, 2 * j + (wave >> 3)) + lanes_below(ge);
+      tie_take |= (uint32_t)(tied && rank < need) << j;
+    }
+  }
+  // taken pages: bit j of `mine`
+  uint32_t mine = 0, wc = 0;
+#pragma unroll
+  for (int j = 0; j < COLS; ++j) {
+    const uint32_t kt = key[j] >> shift;
+    const bool above = radix ? (kt > kprefix || (kt == kprefix && (done || ((tie_take >> j) & 1u)))) : k == C;
+    const bool t = ((cand >> j) & 1u) && above;
+    const unsigned long long g = __ballot(t);
+    wc = lane == j ? (uint32_t)__popcll(g) : wc;
+    mine |= (uint32_t)t << j;
+  }
+  if (lane < COLS) S.cnt[1][lane * kSelWaves + wave] = wc;
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's page-table entries have landed in LDS
+  __syncthreads();
+  const uint32_t P = wave_word_prefix(S.cnt[1], nwords, wave, lane);
+#pragma unroll
+  for (int j = 0; j < COLS; ++j) {
+    const bool t = (mine >> j) & 1u;
+    const unsigned long long g = __ballot(t);
+    // read the word prefix with every lane active: a lane read inside the
+    // branch below may be inactive and hold no defined value
+    const int base = __builtin_amdgcn_readlane((int)P, 2 * j + (wave >> 3));
+    if (t) {
+      const int p = tid + kSelThreads * j;
+      const int o = base + (int)lanes_below(g);
+      if (J.sel) J.sel[o] = p;
+      if (J.work)
+        put_item(J.work, n_pre + o, p, S.sphys[p], max(p * kPage, Pe) - p * kPage,
+                 min(p * kPage + kPage, Ws) - p * kPage);
+    }
+  }
+  // Stores come last: on this target every load wait also waits for earlier stores.
+  if (J.sel)
+    for (int i = k + tid; i < J.budget; i += kSelThreads) J.sel[i] = -1;
+  if (tid == 0 && J.counts) {
+    J.counts[0] = k;
+    J.counts[1] = n_items;
+  }
+  if (J.work) {
+    for (int i = n_items + tid; i < J.max_items; i += kSelThreads) put_item(J.work, i, -1, 0, 0, 0);
+    for (int i = tid; i < n_pre; i += kSelThreads) put_item(J.work, i, i, S.sphys[i], 0, min(kPage, Pe - i * kPage));
+    for (int i = tid; i < n_win; i += kSelThreads) {
+      const int p = w_first + i;
+      put_item(J.work, n_pre + k + i, p, S.sphys[p], max(p * kPage, w0) - p * kPage,
+               min(p * kPage + kPage, L) - p * kPage);
+    }
+  }
+}
+
+}  // namespace fsa
