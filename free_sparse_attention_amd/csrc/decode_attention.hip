@@ -209,16 +209,17 @@ __global__ __launch_bounds__(256, 3) void decode_attention_kernel(
 
 // One workgroup per (sequence, KV head, query head of the group): merges the
 // unit's partials for that head.  Units handled by a single workgroup were
-// finished by the attention kernel.  Every wave redundantly reduces the
-// partials' maxima and sums (no barrier); the 256 threads then sum float4
-// columns over disjoint subsets of partials and merge them in LDS.
+// finished by the attention kernel.  Thread (part, c) owns float4 column c and
+// merges every PARTS-th partial online -- running maximum, rescaled sums -- so
+// each partial's (m, l) and column are loaded together in one round trip; the
+// PARTS states of a column are then merged through LDS.
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, uint16_t* __restrict__ out, int hq, int hkv, int per_wg, int wg_per_unit, int max_seq_len) {
-  constexpr int NQ = D / 4;            // float4 columns of one head
-  constexpr int PARTS = 256 / NQ;      // threads summing disjoint subsets of partials
-  __shared__ float sh_e[kMaxPartials];
+  constexpr int NQ = D / 4;        // float4 columns of one head
+  constexpr int PARTS = 256 / NQ;  // threads sharing a column, each with every PARTS-th partial
+  __shared__ float sh_m[PARTS][NQ], sh_l[PARTS][NQ];
   __shared__ float4 sh_acc[PARTS][NQ];
   const int G = hq / hkv;
   const int unit = blockIdx.x / G, h = blockIdx.x % G;
@@ -231,51 +232,52 @@ __global__ __launch_bounds__(256) void combine_kernel(
     n = ((L + kPage - 1) / kPage + per_wg - 1) / per_wg;
   }
   if (n <= 1) return;  // written directly by the attention kernel
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* ml = part_ml + 2 * (size_t)unit * wg_per_unit * G;
-
-  float M = -INFINITY;
-  for (int w = lane; w < n; w += kWave) M = fmaxf(M, ml[2 * ((size_t)w * G + h)]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float l_loc = 0.f;
-  for (int w = lane; w < n; w += kWave) {
-    const float mw = ml[2 * ((size_t)w * G + h)];
-    const float e = mw == -INFINITY ? 0.f : exp2f(mw - M);
-    if (wave == 0) sh_e[w] = e;
-    l_loc += e * ml[2 * ((size_t)w * G + h) + 1];
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) l_loc += __shfl_xor(l_loc, off);
-  const float Lsum = l_loc;
-  __syncthreads();
-
-  const int c4 = tid % NQ, part = tid / NQ;
+  const int tid = threadIdx.x, c4 = tid % NQ, part = tid / NQ;
+  const float* ml = part_ml + 2 * ((size_t)unit * wg_per_unit * G + h);
   const float4* po = reinterpret_cast<const float4*>(part_o + ((size_t)unit * wg_per_unit * G + h) * D) + c4;
   const size_t wstride = (size_t)G * NQ;  // float4s between consecutive partials
+
+  float M = -INFINITY, Lsum = 0.f;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
+#pragma unroll 8
   for (int w = part; w < n; w += PARTS) {
-    const float e = sh_e[w];
+    const float m = ml[2 * (size_t)w * G];
+    const float l = ml[2 * (size_t)w * G + 1];
     const float4 v = po[(size_t)w * wstride];
-    a.x += e * v.x;
-    a.y += e * v.y;
-    a.z += e * v.z;
-    a.w += e * v.w;
+    const float Mn = fmaxf(M, m);
+    const float ea = M == -INFINITY ? 0.f : exp2f(M - Mn);
+    const float eb = m == -INFINITY ? 0.f : exp2f(m - Mn);
+    a.x = a.x * ea + v.x * eb;
+    a.y = a.y * ea + v.y * eb;
+    a.z = a.z * ea + v.z * eb;
+    a.w = a.w * ea + v.w * eb;
+    Lsum = Lsum * ea + l * eb;
+    M = Mn;
   }
+  sh_m[part][c4] = M;
+  sh_l[part][c4] = Lsum;
   sh_acc[part][c4] = a;
   __syncthreads();
   if (part == 0) {
-    for (int p = 1; p < PARTS; ++p) {
+    float Mt = M;
+#pragma unroll
+    for (int p = 1; p < PARTS; ++p) Mt = fmaxf(Mt, sh_m[p][c4]);
+    float Lt = 0.f;
+    float4 at = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int p = 0; p < PARTS; ++p) {
+      const float mp = sh_m[p][c4];
+      const float e = mp == -INFINITY ? 0.f : exp2f(mp - Mt);
       const float4 v = sh_acc[p][c4];
-      a.x += v.x;
-      a.y += v.y;
-      a.z += v.z;
-      a.w += v.w;
+      at.x += e * v.x;
+      at.y += e * v.y;
+      at.z += e * v.z;
+      at.w += e * v.w;
+      Lt += e * sh_l[p][c4];
     }
-    const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
-    const uint32_t w0 = f32_to_bf16_bits(a.x * inv) | (f32_to_bf16_bits(a.y * inv) << 16);
-    const uint32_t w1 = f32_to_bf16_bits(a.z * inv) | (f32_to_bf16_bits(a.w * inv) << 16);
+    const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;
+    const uint32_t w0 = f32_to_bf16_bits(at.x * inv) | (f32_to_bf16_bits(at.y * inv) << 16);
+    const uint32_t w1 = f32_to_bf16_bits(at.z * inv) | (f32_to_bf16_bits(at.w * inv) << 16);
     *reinterpret_cast<uint2*>(out + ((size_t)b * hq + (size_t)g * G + h) * D + 4 * c4) = make_uint2(w0, w1);
   }
 }
@@ -292,7 +294,7 @@ AttnPlan plan_attention(int units, int max_items) {
   const long total = (long)units * std::max(1, max_items);
   int ipw = (int)((total + round_waves - 1) / round_waves);
   ipw = max(1, min(kMaxItemsPerWave, ipw));
-  // the combine keeps one weight per partial in LDS
+  // bound the partials per unit (the combine walks them in PARTS strands)
   while ((max_items + kAttnWaves * ipw - 1) / (kAttnWaves * ipw) > kMaxPartials) ++ipw;
   AttnPlan p;
   p.items_per_wave = ipw;

@@ -143,7 +143,7 @@ struct AttnPlan {
 
 // Attention work-item sources: every page of the sequence, or the selection's work list.
 enum AttnMode { kDense = 0, kList = 1 };
-constexpr int kMaxPartials = 1024;  // partial results per unit the combine can merge
+constexpr int kMaxPartials = 1024;  // partial results per unit, at most
 
 struct AttnArgs {
   const uint16_t* q;
