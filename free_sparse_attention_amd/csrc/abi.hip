@@ -91,10 +91,13 @@ int max_items_of(const fsa_dims* d, fsa_layer_cfg c, int32_t max_seq_len) {
   return (int)std::max<long>(1, pre + sel + win);
 }
 
-// Workspace of the sparse step: [scores][work][part_ml][part_o]
+// Workspace of the sparse step: [scores][selected items][part_ml][part_o].
+// Partial slots per unit: the prefix/window workgroups of the selection launch
+// first, then the split-K workgroups over the selected items.
 struct SparseWs {
-  size_t scores, work, part_ml, part_o, total;
-  int max_items;
+  size_t scores, sel_work, part_ml, part_o, total;
+  int sel_items, slots;
+  fsa::PwPlan pw;
   fsa::AttnPlan plan;
 };
 
@@ -102,13 +105,15 @@ SparseWs sparse_ws(const fsa_dims* d, fsa_layer_cfg c, int32_t max_seq_len) {
   SparseWs w;
   const size_t units = (size_t)d->batch * d->num_kv_heads;
   const int G = d->num_q_heads / d->num_kv_heads;
-  w.max_items = max_items_of(d, c, max_seq_len);
-  w.plan = fsa::plan_attention((int)units, w.max_items);
+  w.sel_items = std::max(1, std::min(c.budget_pages, n_pages_max(max_seq_len)));
+  w.pw = fsa::plan_prefix_window((int)units, c.prefix_tokens, c.window_tokens, max_seq_len);
+  w.plan = fsa::plan_attention((int)units, w.sel_items);
+  w.slots = w.pw.wg_per_unit + w.plan.wg_per_unit;
   size_t o = 0;
   w.scores = o;   o = align256(o + units * d->max_pages_per_seq * sizeof(float));
-  w.work = o;     o = align256(o + units * w.max_items * 4 * sizeof(int32_t));
-  w.part_ml = o;  o = align256(o + units * w.plan.wg_per_unit * G * 2 * sizeof(float));
-  w.part_o = o;   o = align256(o + units * w.plan.wg_per_unit * G * d->head_dim * sizeof(float));
+  w.sel_work = o; o = align256(o + units * w.sel_items * 4 * sizeof(int32_t));
+  w.part_ml = o;  o = align256(o + units * w.slots * G * 2 * sizeof(float));
+  w.part_o = o;   o = align256(o + units * w.slots * G * d->head_dim * sizeof(float));
   w.total = o;
   return w;
 }
@@ -145,6 +150,8 @@ fsa::AttnArgs attn_args(const fsa_dims* dims, int max_items, float sm_scale, int
   a.work = work;
   a.part_o = part_o;
   a.part_ml = part_ml;
+  a.slots_per_unit = 0;
+  a.slot_base = 0;
   a.out = static_cast<uint16_t*>(out);
   a.batch = dims->batch;
   a.hq = dims->num_q_heads;
@@ -303,16 +310,37 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
                                dims->max_pages_per_seq, cfg.prefix_tokens, cfg.window_tokens,
                                max_seq_len, st),
       "quest_scores launch"));
-  FSA_CHECK(hip_status(
-      fsa::launch_select_pages(at<float>(workspace, w.scores), page_table, seq_lens, sel_pages,
-                               at<int32_t>(workspace, w.work), nullptr, dims->batch, dims->num_kv_heads, dims->max_pages_per_seq,
-                               cfg.prefix_tokens, cfg.window_tokens, cfg.budget_pages, w.max_items,
-                               max_seq_len, st),
-      "select_pages launch"));
-  const fsa::AttnArgs a = attn_args(dims, w.max_items, sm_scale, max_seq_len, q, k_cache, v_cache,
-                                    page_table, seq_lens, at<int32_t>(workspace, w.work),
-                                    at<float>(workspace, w.part_o),
-                                    at<float>(workspace, w.part_ml), out);
+  fsa::StepArgs sa;
+  sa.scores = at<float>(workspace, w.scores);
+  sa.page_table = page_table;
+  sa.seq_lens = seq_lens;
+  sa.sel_pages = sel_pages;
+  sa.sel_work = at<int32_t>(workspace, w.sel_work);
+  sa.sel_items = w.sel_items;
+  sa.batch = dims->batch;
+  sa.hq = dims->num_q_heads;
+  sa.hkv = dims->num_kv_heads;
+  sa.d = dims->head_dim;
+  sa.max_pages = dims->max_pages_per_seq;
+  sa.prefix = cfg.prefix_tokens;
+  sa.window = cfg.window_tokens;
+  sa.budget = cfg.budget_pages;
+  sa.max_seq_len = max_seq_len;
+  sa.q = static_cast<const uint16_t*>(q);
+  sa.kc = static_cast<const uint16_t*>(k_cache);
+  sa.vc = static_cast<const uint16_t*>(v_cache);
+  sa.part_o = at<float>(workspace, w.part_o);
+  sa.part_ml = at<float>(workspace, w.part_ml);
+  sa.slots_per_unit = w.slots;
+  sa.pw_ipw = w.pw.ipw;
+  sa.pw_wg = w.pw.wg_per_unit;
+  sa.scale_log2 = sm_scale * 1.4426950408889634f;
+  FSA_CHECK(hip_status(fsa::launch_select_attend(sa, st), "selection launch"));
+  fsa::AttnArgs a = attn_args(dims, w.sel_items, sm_scale, max_seq_len, q, k_cache, v_cache, page_table, seq_lens,
+                              at<int32_t>(workspace, w.sel_work), at<float>(workspace, w.part_o),
+                              at<float>(workspace, w.part_ml), out);
+  a.slots_per_unit = w.slots;
+  a.slot_base = w.pw.wg_per_unit;
   return hip_status(fsa::launch_attention(fsa::kList, w.plan, a, st), "decode attention launch");
 }
 

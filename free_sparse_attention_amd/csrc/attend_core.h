@@ -1,0 +1,194 @@
+// Per-wave flash-decoding over pages of one (sequence, KV head) and the merge
+// of a workgroup's waves.  Shared by the split-K attention kernel and by the
+// prefix/window attention that runs beside the selection.
+//
+// Per item (one page, a token range [lo, hi) inside it), one wave computes
+//   S^T[token][head] = K[token][:] . q[head][:]     v_mfma_f32_16x16x32_bf16, D/32 steps
+//   online softmax over the page's tokens in fp32 (base-2 exponent, scale folded)
+//   O^T[d][head]    += V^T[d][token] P^T[token][head] v_mfma_f32_16x16x16_bf16, D/16 tiles
+// Heads of the group sit on the N side (zero-padded to 16).  The QK result's
+// register layout (lane (col, gq) holds tokens 4 gq .. 4 gq + 3 of head col)
+// is exactly the B-operand layout the PV product needs, so P never leaves
+// registers.  The cache layouts make every operand load a coalesced read
+// straight from HBM: a K page [D/8][16][8] is read as D/32 contiguous 1 KiB
+// rows, a V page [D][16] as D/16 contiguous 512-byte rows.
+#pragma once
+
+#include "fsa_internal.h"
+
+namespace fsa {
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// Running state of one wave: maximum (log2 domain) and sum per head column,
+// O^T accumulators.
+template <int D>
+struct WaveAttn {
+  float m, l;
+  f32x4_t acc[D / 16];
+};
+
+// LDS for merging WAVES waves' states.
+template <int D, int WAVES>
+struct MergeLds {
+  float o[WAVES][D][17];
+  float m[WAVES][16], l[WAVES][16];
+};
+
+// B operand of QK for head column col of the group: q[col][32 ks + 8 gq .. +8],
+// zero rows beyond G.  q_group points at the group's first query head.
+template <int D>
+__device__ __forceinline__ void load_q_operand(const uint16_t* q_group, int G, bf16x8_t (&qb)[D / 32]) {
+  const int lane = threadIdx.x & 63, col = lane & 15, gq = lane >> 4;
+  const uint16_t* qrow = q_group + (size_t)min(col, G - 1) * D;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    uint4 r = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * gq);
+    if (col >= G) r = make_uint4(0, 0, 0, 0);
+    qb[ks] = __builtin_bit_cast(bf16x8_t, r);
+  }
+}
+
+// One wave attends its first n items; lane j holds item j's pool page and
+// token range.  n must be wave-uniform.  PIPE: two-stage pipeline (the next
+// page's loads in flight while the current page is computed); otherwise one
+// page at a time with fewer registers.  head_off/page_stride locate KV head g
+// of a pool page in both caches.
+template <int D, bool PIPE>
+__device__ __forceinline__ void attend_items(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+                                             size_t head_off, size_t page_stride, const bf16x8_t (&qb)[D / 32],
+                                             int my_phys, int my_lo, int my_hi, int n, float scale_log2,
+                                             WaveAttn<D>& st) {
+  constexpr int NKS = D / 32;  // QK k-steps
+  constexpr int NDT = D / 16;  // PV d-tiles
+  const int lane = threadIdx.x & 63, col = lane & 15, gq = lane >> 4;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) st.acc[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  auto load = [&](int j, uint4 (&kr)[NKS], uint2 (&vr)[NDT]) {
+    const size_t blk = (size_t)__builtin_amdgcn_readlane(my_phys, j) * page_stride + head_off;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      kr[ks] = ld_nt(reinterpret_cast<const uint4*>(kc + blk + (size_t)(64 * ks + lane) * 8));
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+      vr[t] = ld_nt(reinterpret_cast<const uint2*>(vc + blk + (size_t)(16 * t + col) * kPage + 4 * gq));
+  };
+  auto compute = [&](int j, const uint4 (&kr)[NKS], const uint2 (&vr)[NDT]) {
+    const int lo = __builtin_amdgcn_readlane(my_lo, j), hi = __builtin_amdgcn_readlane(my_hi, j);
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[ks]), qb[ks], s, 0, 0, 0);
+    float x[4], mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = 4 * gq + r;
+      x[r] = (tok >= lo && tok < hi) ? s[r] * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, x[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = exp2f(st.m - m_new);
+    float p[4], psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = exp2f(x[r] - m_new);
+      psum += p[r];
+    }
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+    const uint32_t p01 = f32_to_bf16_bits(p[0]) | (f32_to_bf16_bits(p[1]) << 16);
+    const uint32_t p23 = f32_to_bf16_bits(p[2]) | (f32_to_bf16_bits(p[3]) << 16);
+    const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) {
+      st.acc[t] *= alpha;
+      st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, vr[t]), pb, st.acc[t], 0, 0, 0);
+    }
+  };
+
+  if (PIPE) {
+    // Every trip of the loop issues exactly one page of loads and consumes
+    // one, so the number of loads in flight at the loop head is the same on
+    // entry and on the back edge and the compiler waits only for the page
+    // about to be used; the last one or two pages are peeled.
+    uint4 kA[NKS], kB[NKS];
+    uint2 vA[NDT], vB[NDT];
+    if (n > 0) {
+      load(0, kA, vA);
+      int j = 0;
+      for (; j + 2 < n; j += 2) {
+        load(j + 1, kB, vB);
+        compute(j, kA, vA);
+        load(j + 2, kA, vA);
+        compute(j + 1, kB, vB);
+      }
+      if (j + 1 < n) {
+        load(j + 1, kB, vB);
+        compute(j, kA, vA);
+        compute(j + 1, kB, vB);
+      } else {
+        compute(j, kA, vA);
+      }
+    }
+  } else {
+    uint4 kA[NKS];
+    uint2 vA[NDT];
+    for (int j = 0; j < n; ++j) {
+      load(j, kA, vA);
+      compute(j, kA, vA);
+    }
+  }
+  st.l += __shfl_xor(st.l, 16);
+  st.l += __shfl_xor(st.l, 32);
+}
+
+// Merge the WAVES waves of the workgroup through LDS; then each of the G x D
+// values is written either as the bf16 output (direct) or into the partial
+// slot (po: [G][D] sums, pml: [G] (max, sum) pairs).  Waves without items
+// carry m = -inf.
+template <int D, int WAVES>
+__device__ __forceinline__ void merge_waves(MergeLds<D, WAVES>& S, const WaveAttn<D>& st, int G, bool direct,
+                                            uint16_t* __restrict__ out_rows, float* __restrict__ po,
+                                            float* __restrict__ pml) {
+  constexpr int NDT = D / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, gq = lane >> 4;
+  if (gq == 0) {
+    S.m[wave][col] = st.m;
+    S.l[wave][col] = st.l;
+  }
+#pragma unroll
+  for (int t = 0; t < NDT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S.o[wave][16 * t + 4 * gq + r][col] = st.acc[t][r];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += WAVES * kWave) {
+    const int h = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, S.m[w][h]);
+    float o = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      const float mw = S.m[w][h];
+      const float e = mw == -INFINITY ? 0.f : exp2f(mw - M);
+      o += e * S.o[w][d][h];
+      l += e * S.l[w][h];
+    }
+    if (direct) {
+      out_rows[idx] = (uint16_t)f32_to_bf16_bits(l > 0.f ? o / l : 0.f);
+    } else {
+      po[idx] = o;
+      if (d == 0) {
+        pml[2 * h] = M;
+        pml[2 * h + 1] = l;
+      }
+    }
+  }
+}
+
+}  // namespace fsa

@@ -141,6 +141,35 @@ struct AttnPlan {
   int wg_per_unit;     // workgroups launched per (b, KV head)
 };
 
+// One decode step's selection launch: the top-k selection of every (sequence,
+// KV head) plus the attention over its prefix and window pages.
+struct StepArgs {
+  const float* scores;        // [B][Hkv][max_pages] Quest scores
+  const int32_t* page_table;  // [B][max_pages]
+  const int32_t* seq_lens;    // [B]
+  int32_t* sel_pages;         // [B][Hkv][budget] or null
+  int32_t* sel_work;          // [B][Hkv][sel_items][4]: selected items, then empty ones
+  int sel_items;
+  int batch, hq, hkv, d, max_pages, prefix, window, budget, max_seq_len;
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  float* part_o;       // partial slots [B][Hkv][slots_per_unit][G][D]
+  float* part_ml;      // [B][Hkv][slots_per_unit][G][2]
+  int slots_per_unit;  // the prefix/window workgroups take slots [0, pw_wg)
+  int pw_ipw;          // prefix/window items per wave
+  int pw_wg;           // prefix/window workgroups per unit
+  float scale_log2;
+};
+
+// Prefix/window attention plan: at most max_items items per unit, ipw per wave,
+// wg_per_unit 1024-thread workgroups per unit (0 when there are none).
+struct PwPlan {
+  int max_items, ipw, wg_per_unit;
+};
+PwPlan plan_prefix_window(int units, int prefix, int window, int max_seq_len);
+hipError_t launch_select_attend(const StepArgs& a, hipStream_t stream);
+
 // Attention work-item sources: every page of the sequence, or the selection's work list.
 enum AttnMode { kDense = 0, kList = 1 };
 constexpr int kMaxPartials = 1024;  // partial results per unit, at most
@@ -154,6 +183,8 @@ struct AttnArgs {
   const int32_t* work;    // selection work items (kList)
   float* part_o;
   float* part_ml;
+  int slots_per_unit;  // partial slots per unit in part_o/part_ml; 0: the plan's workgroups
+  int slot_base;       // first slot of this launch's workgroups (with slots_per_unit > 0)
   uint16_t* out;
   int batch, hq, hkv, d, max_pages, max_items;
   float scale_log2;

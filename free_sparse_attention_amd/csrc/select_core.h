@@ -73,6 +73,8 @@ struct SelectJob {
   int32_t* work;    // the unit's work list, or null
   int32_t* sel;     // the unit's selected pages, or null
   int32_t* counts;  // the unit's (k, items), or null
+  int32_t* sel_work;  // or null: the selected items alone, (page, pool page, lo, hi) at [o],
+  int sel_items;      // padded with empty items up to sel_items
 };
 
 __device__ __forceinline__ void put_item(int32_t* work, int idx, int p, int phys, int lo, int hi) {
@@ -265,6 +267,7 @@ __device__ __forceinline__ void select_unit(SelectLds& S, const SelectJob& J) {
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's page-table entries have landed in LDS
   __syncthreads();
   const uint32_t P = wave_word_prefix(S.cnt[1], nwords, wave, lane);
+  int32_t* selw = J.sel_work ? J.sel_work : (J.work ? J.work + 4 * n_pre : nullptr);  // item o of the selection
 #pragma unroll
   for (int j = 0; j < COLS; ++j) {
     const bool t = (mine >> j) & 1u;
@@ -276,9 +279,8 @@ __device__ __forceinline__ void select_unit(SelectLds& S, const SelectJob& J) {
       const int p = tid + kSelThreads * j;
       const int o = base + (int)lanes_below(g);
       if (J.sel) J.sel[o] = p;
-      if (J.work)
-        put_item(J.work, n_pre + o, p, S.sphys[p], max(p * kPage, Pe) - p * kPage,
-                 min(p * kPage + kPage, Ws) - p * kPage);
+      if (selw)
+        put_item(selw, o, p, S.sphys[p], max(p * kPage, Pe) - p * kPage, min(p * kPage + kPage, Ws) - p * kPage);
     }
   }
   // Stores come last: on this target every load wait also waits for earlier stores.
@@ -288,6 +290,8 @@ __device__ __forceinline__ void select_unit(SelectLds& S, const SelectJob& J) {
     J.counts[0] = k;
     J.counts[1] = n_items;
   }
+  if (J.sel_work)
+    for (int i = k + tid; i < J.sel_items; i += kSelThreads) put_item(J.sel_work, i, -1, 0, 0, 0);
   if (J.work) {
     for (int i = n_items + tid; i < J.max_items; i += kSelThreads) put_item(J.work, i, -1, 0, 0, 0);
     for (int i = tid; i < n_pre; i += kSelThreads) put_item(J.work, i, i, S.sphys[i], 0, min(kPage, Pe - i * kPage));

@@ -1,6 +1,21 @@
-// Stand-alone top-k page selection and merge with the prefix and the window:
-// one 1024-thread workgroup per (sequence, KV head) runs the selection of
-// select_core.h on scores in memory.
+// Top-k page selection (select_core.h), stand-alone and as part of the decode
+// step.
+//
+// Stand-alone: one 1024-thread workgroup per (sequence, KV head) selects and
+// writes the full work list (prefix, selected and window items).
+//
+// In the decode step the selection occupies one CU per (sequence, KV head)
+// for a few microseconds and needs little memory bandwidth, while the prefix
+// and window pages -- attended whatever the selection decides -- are known
+// from the sequence length alone.  So the same launch carries further
+// 1024-thread workgroups that attend the prefix and window pages on the other
+// CUs (16 waves, each walking a few pages with the flash-decoding of
+// attend_core.h, merged through LDS into one partial per workgroup).  The
+// selection then writes only the selected items, which the split-K attention
+// kernel attends next; the combine merges both kinds of partials.
+#include <algorithm>
+
+#include "attend_core.h"
 #include "select_core.h"
 
 namespace fsa {
@@ -27,7 +42,90 @@ __global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
   J.work = work ? work + 4 * (size_t)unit * max_items : nullptr;
   J.sel = sel_pages ? sel_pages + (size_t)unit * budget : nullptr;
   J.counts = counts ? counts + 2 * unit : nullptr;
+  J.sel_work = nullptr;
+  J.sel_items = 0;
   select_unit<COLS>(S, J);
+}
+
+// Attention over the prefix and window pages of one unit: pages [0, n_pre)
+// and [w_first, ceil(L / 16)), item i of the unit's list being prefix page i
+// for i < n_pre, else window page w_first + i - n_pre.  Wave w of workgroup wg
+// takes items (16 wg + w) ipw + [0, ipw).
+template <int D>
+__device__ __forceinline__ void prefix_window_attend(MergeLds<D, kSelWaves>& S, const StepArgs& A, int unit,
+                                                     int wg) {
+  const int b = unit / A.hkv, g = unit % A.hkv, G = A.hq / A.hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = (wg * kSelWaves + wave) * A.pw_ipw + lane;
+  const int32_t* pt = A.page_table + (size_t)b * A.max_pages;
+  // Item i of a sequence of length L: page, token range (lo, hi empty if none).
+  auto item = [&](int L, int& p, int& lo, int& hi) {
+    const int Pe = min(A.prefix, L), Ws = max(0, L - A.window);
+    const int n_pre = (Pe + kPage - 1) / kPage;
+    const int w0 = max(Ws, Pe);
+    const int w_first = w0 / kPage, n_pages = (L + kPage - 1) / kPage;
+    const int n_win = (L > w0) ? n_pages - w_first : 0;
+    p = 0;
+    lo = hi = 0;
+    if (lane >= A.pw_ipw || i >= n_pre + n_win) return;
+    if (i < n_pre) {
+      p = i;
+      hi = min(kPage, Pe - p * kPage);
+    } else {
+      p = w_first + i - n_pre;
+      lo = max(p * kPage, w0) - p * kPage;
+      hi = min(p * kPage + kPage, L) - p * kPage;
+    }
+  };
+  // The page-table entry is loaded for the item the host-side length bound
+  // implies, together with the length itself and q; it is loaded again only
+  // where the actual length moves the item to another page.
+  int p_guess, lo, hi;
+  item(A.max_seq_len, p_guess, lo, hi);
+  int my_phys = pt[p_guess];
+  bf16x8_t qb[D / 32];
+  load_q_operand<D>(A.q + ((size_t)b * A.hq + (size_t)g * G) * D, G, qb);
+  const int L = min(A.seq_lens[b], A.max_seq_len);
+  int p, my_lo, my_hi;
+  item(L, p, my_lo, my_hi);
+  if (my_lo < my_hi && p != p_guess) my_phys = pt[p];
+  const int n = __popcll(__ballot(my_lo < my_hi));  // a prefix of the wave's lanes
+  WaveAttn<D> st;
+  attend_items<D, false>(A.kc, A.vc, (size_t)g * (kPage * D), (size_t)A.hkv * (kPage * D), qb, my_phys, my_lo,
+                         my_hi, n, A.scale_log2, st);
+  const size_t slot = (size_t)unit * A.slots_per_unit + wg;
+  merge_waves<D, kSelWaves>(S, st, G, false, nullptr, A.part_o + slot * G * D, A.part_ml + 2 * slot * G);
+}
+
+template <int COLS, int D>
+__global__ __launch_bounds__(kSelThreads) void select_attend_kernel(const StepArgs A) {
+  __shared__ union {
+    SelectLds sel;
+    MergeLds<D, kSelWaves> att;
+  } U;
+  const int units = A.batch * A.hkv;
+  if ((int)blockIdx.x < units) {
+    const int unit = blockIdx.x, b = unit / A.hkv;
+    SelectJob J;
+    J.scores = A.scores + (size_t)unit * A.max_pages;
+    J.pt = A.page_table + (size_t)b * A.max_pages;
+    J.seq_len = A.seq_lens + b;
+    J.minmax = nullptr;
+    J.max_seq_len = A.max_seq_len;
+    J.prefix = A.prefix;
+    J.window = A.window;
+    J.budget = A.budget;
+    J.max_items = 0;
+    J.work = nullptr;
+    J.sel = A.sel_pages ? A.sel_pages + (size_t)unit * A.budget : nullptr;
+    J.counts = nullptr;
+    J.sel_work = A.sel_work + 4 * (size_t)unit * A.sel_items;
+    J.sel_items = A.sel_items;
+    select_unit<COLS>(U.sel, J);
+  } else {
+    const int w = blockIdx.x - units;
+    prefix_window_attend<D>(U.att, A, w / A.pw_wg, w % A.pw_wg);
+  }
 }
 
 }  // namespace
@@ -52,6 +150,48 @@ hipError_t launch_select_pages(const float* scores, const int32_t* page_table,
     default: FSA_SEL(32); break;
   }
 #undef FSA_SEL
+  return hipGetLastError();
+}
+
+PwPlan plan_prefix_window(int units, int prefix, int window, int max_seq_len) {
+  const int n_max = (max_seq_len + kPage - 1) / kPage;
+  const int pre = std::min((prefix + kPage - 1) / kPage, n_max);
+  const int win = std::min((window + kPage - 1) / kPage + 1, n_max);
+  PwPlan p;
+  p.max_items = std::min(pre + win, n_max);
+  if (p.max_items == 0) {
+    p.ipw = 1;
+    p.wg_per_unit = 0;
+    return p;
+  }
+  // one workgroup per CU (the launch's LDS), the CUs beside the selection's
+  const long waves = (long)std::max(1, device_cu_count() - units) * kSelWaves;
+  const long need = (long)units * p.max_items;
+  p.ipw = (int)std::max<long>(1, std::min<long>(kWave, (need + waves - 1) / waves));
+  p.wg_per_unit = (p.max_items + kSelWaves * p.ipw - 1) / (kSelWaves * p.ipw);
+  return p;
+}
+
+hipError_t launch_select_attend(const StepArgs& a, hipStream_t stream) {
+  const unsigned grid = (unsigned)(a.batch * a.hkv * (1 + a.pw_wg));
+#define FSA_SA(C, DD) hipLaunchKernelGGL((select_attend_kernel<C, DD>), dim3(grid), dim3(kSelThreads), 0, stream, a)
+#define FSA_SA_D(C)         \
+  do {                      \
+    if (a.d == 128)         \
+      FSA_SA(C, 128);       \
+    else                    \
+      FSA_SA(C, 64);        \
+  } while (0)
+  switch (select_cols(a.max_seq_len)) {
+    case 1: FSA_SA_D(1); break;
+    case 2: FSA_SA_D(2); break;
+    case 4: FSA_SA_D(4); break;
+    case 8: FSA_SA_D(8); break;
+    case 16: FSA_SA_D(16); break;
+    default: FSA_SA_D(32); break;
+  }
+#undef FSA_SA_D
+#undef FSA_SA
   return hipGetLastError();
 }
 
