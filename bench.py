@@ -114,7 +114,7 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
 
     dev = torch.device("cuda:0")
     score_bytes, step_bytes = alg_bytes(wl)
-    R = max(2, math.ceil(2 * MALL_BYTES / step_bytes))
+    R = min(128, max(2, math.ceil(2 * MALL_BYTES / step_bytes)))
     log(f"[bench] {wl.name}: uploading, {R} cache replicas")
     base = DeviceWorkload(wl, device=dev)
     reps = [(base.k_cache, base.v_cache, base.meta)]
@@ -181,6 +181,29 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
     return res
 
 
+SWEEP_LENS = (2048, 4096, 8192, 16384, 32768, 65536, 131072, 262144)
+
+
+def crossover_sweep(steps, warmup):
+    """Sparse and dense step times at the 64k workload's shapes (batch 4, Hq 16 / Hkv 4,
+    D 128, prefix 128, window 1024, budget 128 pages) for context lengths 2k..256k."""
+    import synth
+    rows = []
+    for L in SWEEP_LENS:
+        wl = synth.make_workload("ctx64k", seq_lens=(L,) * 4)
+        P, W, budget = wl.cfg
+        Pe, Ws = min(P, L), max(0, L - W)
+        C = (-(-Ws // wl.page) - Pe // wl.page) if Pe < Ws else 0
+        r = measure(wl, steps, warmup, with_dense=True, reps_kernel=20)
+        rows.append({"seq_len": L, "candidate_pages": C,
+                     "path": "dense (every candidate fits the budget)" if C <= budget else "sparse",
+                     "sparse_us": 1000.0 * r["ms_per_step"], "dense_us": 1000.0 * r["dense_ms_per_step"],
+                     "speedup_vs_dense": r["speedup_vs_dense"], "step_GBps": r["step_GBps"]})
+        log(f"[sweep] L={L}: sparse {rows[-1]['sparse_us']:.1f} us, dense {rows[-1]['dense_us']:.1f} us")
+        del wl
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,6 +213,8 @@ def main():
     ap.add_argument("--no-also", action="store_true", help="skip the 256k measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead: sparse vs dense step time for context lengths 2k..256k")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU; this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -199,6 +224,15 @@ def main():
     synth.lib()
     import free_sparse_attention_amd as fsa
     fsa.load()
+
+    if args.sweep:
+        rows = crossover_sweep(max(20, args.steps // 4), args.warmup)
+        print(json.dumps({"metric": "sparse vs dense decode step time by context length", "unit": "us",
+                          "n_gpus": 1, "data": "synthetic (seeded; needles planted)",
+                          "config": {"workload": "ctx64k shapes", "batch": 4, "q_heads": 16, "kv_heads": 4,
+                                     "head_dim": 128, "prefix": 128, "window": 1024, "budget_pages": 128},
+                          "sweep": rows}), flush=True)
+        return
 
     t0 = time.time()
     wl = synth.make_workload(args.workload)

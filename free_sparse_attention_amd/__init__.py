@@ -23,4 +23,5 @@ from ._lib import (  # noqa: F401
     select_pages,
     sparse_decode_attn,
     sparse_decode_workspace_bytes,
+    validate_inputs,
 )

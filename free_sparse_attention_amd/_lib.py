@@ -22,7 +22,7 @@ EXPORTED = (
     "fsa_last_error", "fsa_import_kv_plain", "fsa_append_kv", "fsa_build_page_meta", "fsa_meta_bytes",
     "fsa_quest_scores", "fsa_max_work_items", "fsa_select_pages",
     "fsa_sparse_decode_workspace_bytes", "fsa_sparse_decode_attn",
-    "fsa_dense_decode_workspace_bytes", "fsa_dense_decode_attn",
+    "fsa_dense_decode_workspace_bytes", "fsa_dense_decode_attn", "fsa_validate_inputs",
 )
 
 
@@ -72,6 +72,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             "fsa_sparse_decode_attn": (i32, [D, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "fsa_dense_decode_workspace_bytes": (sz, [D, i32]),
             "fsa_dense_decode_attn": (i32, [D, f32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "fsa_validate_inputs": (i32, [D, i32, vp, vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -192,3 +193,12 @@ def dense_decode_attn(d: Dims, sm_scale, max_seq_len, q, k_cache, v_cache, page_
         _p(v_cache, "v_cache", 2), _i32(page_table, "page_table"), _i32(seq_lens, "seq_lens"),
         _p(out, "out", 2), _p(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+def validate_inputs(d: Dims, max_seq_len, q, page_table, seq_lens, scratch=None, stream=None) -> None:
+    """Debug check of device inputs (synchronises); raises FsaError naming a violation."""
+    if scratch is None:
+        scratch = torch.empty(4, dtype=torch.int32, device=page_table.device)
+    _check(load().fsa_validate_inputs(
+        ctypes.byref(d), int(max_seq_len), _p(q, "q", 2) if q is not None else None,
+        _i32(page_table, "page_table"), _i32(seq_lens, "seq_lens"), _i32(scratch, "scratch"), _stream(stream)))

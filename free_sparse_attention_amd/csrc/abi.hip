@@ -91,12 +91,23 @@ int max_items_of(const fsa_dims* d, fsa_layer_cfg c, int32_t max_seq_len) {
   return (int)std::max<long>(1, pre + sel + win);
 }
 
+// Candidate pages of a sequence of length L: pages meeting [min(P, L), L - W).
+// Nondecreasing in L, so its value at the host bound bounds every sequence.
+int candidate_pages(fsa_layer_cfg c, int32_t L) {
+  const int Pe = std::min(c.prefix_tokens, L), Ws = std::max(0, L - c.window_tokens);
+  return Pe < Ws ? (Ws + fsa::kPage - 1) / fsa::kPage - Pe / fsa::kPage : 0;
+}
+
 // Workspace of the sparse step: [scores][selected items][part_ml][part_o].
 // Partial slots per unit: the prefix/window workgroups of the selection launch
-// first, then the split-K workgroups over the selected items.
+// first, then the split-K workgroups over the selected items.  When no
+// sequence can have more candidate pages than the budget, every candidate is
+// taken, the attended set is the whole sequence and the step runs the dense
+// kernels: [scores][part_ml][part_o] with the dense plan.
 struct SparseWs {
   size_t scores, sel_work, part_ml, part_o, total;
   int sel_items, slots;
+  bool all_taken;
   fsa::PwPlan pw;
   fsa::AttnPlan plan;
 };
@@ -105,13 +116,22 @@ SparseWs sparse_ws(const fsa_dims* d, fsa_layer_cfg c, int32_t max_seq_len) {
   SparseWs w;
   const size_t units = (size_t)d->batch * d->num_kv_heads;
   const int G = d->num_q_heads / d->num_kv_heads;
-  w.sel_items = std::max(1, std::min(c.budget_pages, n_pages_max(max_seq_len)));
-  w.pw = fsa::plan_prefix_window((int)units, c.prefix_tokens, c.window_tokens, max_seq_len);
-  w.plan = fsa::plan_attention((int)units, w.sel_items);
-  w.slots = w.pw.wg_per_unit + w.plan.wg_per_unit;
+  w.all_taken = candidate_pages(c, max_seq_len) <= c.budget_pages;
   size_t o = 0;
   w.scores = o;   o = align256(o + units * d->max_pages_per_seq * sizeof(float));
-  w.sel_work = o; o = align256(o + units * w.sel_items * 4 * sizeof(int32_t));
+  if (w.all_taken) {
+    w.sel_items = 0;
+    w.pw = fsa::PwPlan{0, 1, 0};
+    w.plan = fsa::plan_attention((int)units, n_pages_max(max_seq_len));
+    w.slots = w.plan.wg_per_unit;
+    w.sel_work = o;
+  } else {
+    w.sel_items = std::max(1, std::min(c.budget_pages, n_pages_max(max_seq_len)));
+    w.pw = fsa::plan_prefix_window((int)units, c.prefix_tokens, c.window_tokens, max_seq_len);
+    w.plan = fsa::plan_attention((int)units, w.sel_items);
+    w.slots = w.pw.wg_per_unit + w.plan.wg_per_unit;
+    w.sel_work = o; o = align256(o + units * w.sel_items * 4 * sizeof(int32_t));
+  }
   w.part_ml = o;  o = align256(o + units * w.slots * G * 2 * sizeof(float));
   w.part_o = o;   o = align256(o + units * w.slots * G * d->head_dim * sizeof(float));
   w.total = o;
@@ -303,6 +323,21 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
   if (!workspace || workspace_bytes < w.total)
     return fail(FSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, w.total);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (w.all_taken) {
+    // every candidate page is selected: the attended set is [0, L), i.e. dense
+    // attention; the selection runs only to report the selected pages (it
+    // takes all candidates without looking at scores)
+    if (sel_pages)
+      FSA_CHECK(hip_status(fsa::launch_select_pages(at<float>(workspace, w.scores), page_table, seq_lens, sel_pages,
+                                                    nullptr, nullptr, dims->batch, dims->num_kv_heads,
+                                                    dims->max_pages_per_seq, cfg.prefix_tokens, cfg.window_tokens,
+                                                    cfg.budget_pages, 0, max_seq_len, st),
+                           "select_pages launch"));
+    const fsa::AttnArgs a = attn_args(dims, n_pages_max(max_seq_len), sm_scale, max_seq_len, q, k_cache, v_cache,
+                                      page_table, seq_lens, nullptr, at<float>(workspace, w.part_o),
+                                      at<float>(workspace, w.part_ml), out);
+    return hip_status(fsa::launch_attention(fsa::kDense, w.plan, a, st), "dense decode attention launch");
+  }
   FSA_CHECK(hip_status(
       fsa::launch_quest_scores(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(meta),
                                seq_lens, at<float>(workspace, w.scores), dims->batch,
@@ -370,6 +405,35 @@ fsa_status fsa_dense_decode_attn(const fsa_dims* dims, float sm_scale, int32_t m
                                     at<float>(workspace, w.part_ml), out);
   return hip_status(fsa::launch_attention(fsa::kDense, w.plan, a, static_cast<hipStream_t>(stream)),
                     "dense decode attention launch");
+}
+
+fsa_status fsa_validate_inputs(const fsa_dims* dims, int32_t max_seq_len, const void* q,
+                               const int32_t* page_table, const int32_t* seq_lens, int32_t* scratch,
+                               void* stream) {
+  FSA_CHECK(check_dims(dims));
+  FSA_CHECK(check_len(dims, max_seq_len));
+  FSA_CHECK(need(page_table, "page_table"));
+  FSA_CHECK(need(seq_lens, "seq_lens"));
+  FSA_CHECK(need(scratch, "scratch"));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  FSA_CHECK(hip_status(fsa::launch_validate(static_cast<const uint16_t*>(q), page_table, seq_lens, scratch,
+                                            dims->batch, q ? dims->num_q_heads : 0, dims->head_dim,
+                                            dims->max_pages_per_seq, dims->num_pool_pages, max_seq_len, st),
+                       "validate launch"));
+  int32_t h[4];
+  FSA_CHECK(hip_status(hipMemcpyAsync(h, scratch, sizeof(h), hipMemcpyDeviceToHost, st), "validate copy"));
+  FSA_CHECK(hip_status(hipStreamSynchronize(st), "validate sync"));
+  if (h[0] == 0) return FSA_OK;
+  switch (h[1]) {
+    case 1:
+      return fail(FSA_ERR_INVALID_ARG, "%d invalid inputs; e.g. seq_lens[%d] = %d outside [1, %d]", h[0], h[2], h[3],
+                  max_seq_len);
+    case 2:
+      return fail(FSA_ERR_INVALID_ARG, "%d invalid inputs; e.g. page_table[%d][%d] outside [0, %d)", h[0], h[2], h[3],
+                  dims->num_pool_pages);
+    default:
+      return fail(FSA_ERR_INVALID_ARG, "%d invalid inputs; e.g. q element %d is not finite", h[0], h[2]);
+  }
 }
 
 }  // extern "C"

@@ -185,6 +185,19 @@ fsa_status fsa_dense_decode_attn(const fsa_dims* dims, float sm_scale, int32_t m
                                  const int32_t* page_table, const int32_t* seq_lens, void* out,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Debug check of the device-resident inputs of a decode step; unlike every
+ * other call it synchronises `stream` and is not graph-capturable.  Checks
+ * that every seq_lens[b] lies in [1, max_seq_len], that page_table[b][p] lies
+ * in [0, num_pool_pages) for every page p < ceil(seq_lens[b] / S) in use, and
+ * that every value of q (bf16 [B][Hq][D], device; may be NULL to skip) is
+ * finite.  The other entry points trust these values.
+ *   scratch  int32[4] (device), caller-owned, no initial contents needed
+ * Returns FSA_OK, or FSA_ERR_INVALID_ARG with fsa_last_error() naming the
+ * number of violations and one of them. */
+fsa_status fsa_validate_inputs(const fsa_dims* dims, int32_t max_seq_len, const void* q,
+                               const int32_t* page_table, const int32_t* seq_lens, int32_t* scratch,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -269,3 +269,27 @@ def _tokens_at(wl, lens, n):
         kn[b] = synth.core.fill_tokens(kk, b, int(lens[b]), n, wl.hkv, wl.d, wl.k_scale)
         vn[b] = synth.core.fill_tokens(kv, b, int(lens[b]), n, wl.hkv, wl.d, None)
     return kn, vn
+
+
+# ------------------------------------------------------------------ input validation
+
+def test_validate_inputs_names_the_violation():
+    """The debug validator accepts the workload's inputs and reports a length
+    out of range, a page-table entry outside the pool and a non-finite query.
+    It only reads these values; nothing else runs on the corrupted copies."""
+    import free_sparse_attention_amd as fsa
+    wl = synth.make_workload("tiny")
+    dw = DeviceWorkload(wl, build_meta=False)
+    fsa.validate_inputs(dw.dims, dw.max_seq_len, dw.q, dw.page_table, dw.seq_lens)
+    bad_len = dw.seq_lens.clone()
+    bad_len[0] = dw.max_seq_len + 1
+    with pytest.raises(fsa.FsaError, match="seq_lens"):
+        fsa.validate_inputs(dw.dims, dw.max_seq_len, dw.q, dw.page_table, bad_len)
+    bad_pt = dw.page_table.clone()
+    bad_pt[0, 5] = wl.pool_pages
+    with pytest.raises(fsa.FsaError, match=r"page_table\[0\]\[5\]"):
+        fsa.validate_inputs(dw.dims, dw.max_seq_len, dw.q, bad_pt, dw.seq_lens)
+    bad_q = dw.q.clone()
+    bad_q.view(-1)[77] = float("nan")
+    with pytest.raises(fsa.FsaError, match="q element 77"):
+        fsa.validate_inputs(dw.dims, dw.max_seq_len, bad_q, dw.page_table, dw.seq_lens)
