@@ -46,16 +46,15 @@ __global__ __launch_bounds__(256) void quest_score_kernel(
   constexpr int NSTEP = 2 * D / 32;  // k-steps over the 2D metadata values
   const int unit = blockIdx.x / wg_per_unit, wg = blockIdx.x % wg_per_unit;
   const int b = unit / hkv, g = unit % hkv, G = hq / hkv;
-  const int L = min(seq_lens[b], max_seq_len);  // lengths beyond the host bound are clamped
-  const int Pe = min(prefix, L), Ws = max(0, L - window);
-  if (Pe >= Ws) return;
-  const int c_lo = Pe / kPage, c_hi = (Ws + kPage - 1) / kPage;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, gq = lane >> 4;
-  const int t_first = c_lo / kMetaTile + (wg * 4 + wave) * tiles_per_wave;
-  const int t_end = (c_hi + kMetaTile - 1) / kMetaTile;
-  if (t_first >= t_end) return;
-  const int n_tiles = min(tiles_per_wave, t_end - t_first);
+  // Every sequence with candidates has L > prefix, so its candidates start at
+  // page prefix / 16 and end at or before the host bound's: the wave's first
+  // tile is known before the length arrives and is loaded together with it.
+  const int c_lo_h = min(prefix, max_seq_len) / kPage;
+  const int c_hi_h = (max(0, max_seq_len - window) + kPage - 1) / kPage;
+  const int t_first = c_lo_h / kMetaTile + (wg * 4 + wave) * tiles_per_wave;
+  const int t_end_h = max(1, (c_hi_h + kMetaTile - 1) / kMetaTile);
 
   // A operand: row `col` = query head col of the group (zero beyond G).
   bf16x8_t a[NSTEP];
@@ -76,6 +75,20 @@ __global__ __launch_bounds__(256) void quest_score_kernel(
   const int tiles = meta_tiles(max_pages);
   const uint16_t* mbase = meta + (size_t)unit * tiles * (NSTEP * kMetaTile * 32) + col * 32 + 8 * gq;
   float* srow = scores + (size_t)unit * max_pages;
+  uint4 bufA[NSTEP], bufB[NSTEP];
+  {
+    // first tile, clamped into the host bound's range (used only if valid below)
+    const uint16_t* src = mbase + (size_t)min(t_first, t_end_h - 1) * (NSTEP * kMetaTile * 32);
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) bufA[s] = *reinterpret_cast<const uint4*>(src + s * (kMetaTile * 32));
+  }
+  const int L = min(seq_lens[b], max_seq_len);  // lengths beyond the host bound are clamped
+  const int Pe = min(prefix, L), Ws = max(0, L - window);
+  if (Pe >= Ws) return;
+  const int c_lo = Pe / kPage, c_hi = (Ws + kPage - 1) / kPage;  // c_lo == c_lo_h here
+  const int t_end = (c_hi + kMetaTile - 1) / kMetaTile;
+  if (t_first >= t_end) return;
+  const int n_tiles = min(tiles_per_wave, t_end - t_first);
   // Loads are unconditional (tiles are whole; pages outside the candidates
   // are scored but not stored), so the number of loads in flight is the same
   // on every path and the compiler waits only for the tile about to be reduced.
@@ -100,8 +113,6 @@ __global__ __launch_bounds__(256) void quest_score_kernel(
     if (gq == 0 && p >= c_lo && p < c_hi) srow[p] = sc;
   };
 
-  uint4 bufA[NSTEP], bufB[NSTEP];
-  load(0, bufA);
   int t = 0;
   for (; t + 2 < n_tiles; t += 2) {
     load(t + 1, bufB);
