@@ -98,42 +98,45 @@ int candidate_pages(fsa_layer_cfg c, int32_t L) {
   return Pe < Ws ? (Ws + fsa::kPage - 1) / fsa::kPage - Pe / fsa::kPage : 0;
 }
 
-// Workspace of the sparse step: [scores][selected items][part_ml][part_o].
-// Partial slots per unit: the prefix/window workgroups of the selection launch
-// first, then the split-K workgroups over the selected items.  When no
-// sequence can have more candidate pages than the budget, every candidate is
-// taken, the attended set is the whole sequence and the step runs the dense
-// kernels: [scores][part_ml][part_o] with the dense plan.
+// Workspace of the sparse step: [scores][selected items (narrow plan)]
+// [part_ml][part_o].  Partial slots per unit: wide plan, one per selection
+// replica; narrow plan, the prefix/window workgroups first, then the split-K
+// workgroups over the selected items.  When no sequence can have more
+// candidate pages than the budget, every candidate is taken, the attended set
+// is the whole sequence and the step runs the dense kernels (dense plan).
 struct SparseWs {
   size_t scores, sel_work, part_ml, part_o, total;
-  int sel_items, slots;
+  int slots;
   bool all_taken;
-  fsa::PwPlan pw;
-  fsa::AttnPlan plan;
+  fsa::StepPlan step;
+  fsa::AttnPlan plan;  // dense plan (all candidates taken) or split-K plan (narrow)
 };
 
 SparseWs sparse_ws(const fsa_dims* d, fsa_layer_cfg c, int32_t max_seq_len) {
   SparseWs w;
-  const size_t units = (size_t)d->batch * d->num_kv_heads;
+  const int units = d->batch * d->num_kv_heads;
   const int G = d->num_q_heads / d->num_kv_heads;
   w.all_taken = candidate_pages(c, max_seq_len) <= c.budget_pages;
   size_t o = 0;
-  w.scores = o;   o = align256(o + units * d->max_pages_per_seq * sizeof(float));
+  w.scores = o;   o = align256(o + (size_t)units * d->max_pages_per_seq * sizeof(float));
+  w.sel_work = o;
   if (w.all_taken) {
-    w.sel_items = 0;
-    w.pw = fsa::PwPlan{0, 1, 0};
-    w.plan = fsa::plan_attention((int)units, n_pages_max(max_seq_len));
+    w.step = fsa::StepPlan{0, 0, 0, fsa::PwPlan{0, 1, 0}};
+    w.plan = fsa::plan_attention(units, n_pages_max(max_seq_len));
     w.slots = w.plan.wg_per_unit;
-    w.sel_work = o;
   } else {
-    w.sel_items = std::max(1, std::min(c.budget_pages, n_pages_max(max_seq_len)));
-    w.pw = fsa::plan_prefix_window((int)units, c.prefix_tokens, c.window_tokens, max_seq_len);
-    w.plan = fsa::plan_attention((int)units, w.sel_items);
-    w.slots = w.pw.wg_per_unit + w.plan.wg_per_unit;
-    w.sel_work = o; o = align256(o + units * w.sel_items * 4 * sizeof(int32_t));
+    w.step = fsa::plan_step(units, c.prefix_tokens, c.window_tokens, c.budget_pages, max_seq_len);
+    if (w.step.sel_rep > 0) {
+      w.plan = fsa::AttnPlan{0, 0};
+      w.slots = w.step.sel_rep;
+    } else {
+      w.plan = fsa::plan_attention(units, w.step.sel_items);
+      w.slots = w.step.pw.wg_per_unit + w.plan.wg_per_unit;
+      o = align256(o + (size_t)units * w.step.sel_items * 4 * sizeof(int32_t));
+    }
   }
-  w.part_ml = o;  o = align256(o + units * w.slots * G * 2 * sizeof(float));
-  w.part_o = o;   o = align256(o + units * w.slots * G * d->head_dim * sizeof(float));
+  w.part_ml = o;  o = align256(o + (size_t)units * w.slots * G * 2 * sizeof(float));
+  w.part_o = o;   o = align256(o + (size_t)units * w.slots * G * d->head_dim * sizeof(float));
   w.total = o;
   return w;
 }
@@ -350,8 +353,10 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
   sa.page_table = page_table;
   sa.seq_lens = seq_lens;
   sa.sel_pages = sel_pages;
+  sa.sel_rep = w.step.sel_rep;
+  sa.per = w.step.per;
   sa.sel_work = at<int32_t>(workspace, w.sel_work);
-  sa.sel_items = w.sel_items;
+  sa.sel_items = w.step.sel_items;
   sa.batch = dims->batch;
   sa.hq = dims->num_q_heads;
   sa.hkv = dims->num_kv_heads;
@@ -367,15 +372,16 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
   sa.part_o = at<float>(workspace, w.part_o);
   sa.part_ml = at<float>(workspace, w.part_ml);
   sa.slots_per_unit = w.slots;
-  sa.pw_ipw = w.pw.ipw;
-  sa.pw_wg = w.pw.wg_per_unit;
+  sa.pw_ipw = w.step.pw.ipw;
+  sa.pw_wg = w.step.pw.wg_per_unit;
   sa.scale_log2 = sm_scale * 1.4426950408889634f;
   FSA_CHECK(hip_status(fsa::launch_select_attend(sa, st), "selection launch"));
-  fsa::AttnArgs a = attn_args(dims, w.sel_items, sm_scale, max_seq_len, q, k_cache, v_cache, page_table, seq_lens,
+  fsa::AttnArgs a = attn_args(dims, w.step.sel_items, sm_scale, max_seq_len, q, k_cache, v_cache, page_table, seq_lens,
                               at<int32_t>(workspace, w.sel_work), at<float>(workspace, w.part_o),
                               at<float>(workspace, w.part_ml), out);
+  if (w.step.sel_rep > 0) return hip_status(fsa::launch_combine(a, w.slots, st), "combine launch");
   a.slots_per_unit = w.slots;
-  a.slot_base = w.pw.wg_per_unit;
+  a.slot_base = w.step.pw.wg_per_unit;
   return hip_status(fsa::launch_attention(fsa::kList, w.plan, a, st), "decode attention launch");
 }
 

@@ -95,14 +95,14 @@ __global__ __launch_bounds__(256) void combine_kernel(
   const int G = hq / hkv;
   const int unit = blockIdx.x / G, h = blockIdx.x % G;
   const int b = unit / hkv, g = unit % hkv;
-  // partial slots in use: a work list fills all of them (empty ones carry
-  // m = -inf); dense units use as many as their length needs
+  // partial slots in use: all of them for the decode step's partials (empty
+  // ones carry m = -inf); dense units use as many as their length needs
   int n = slots_per_unit;
   if (MODE == kDense) {
     const int L = min(seq_lens[b], max_seq_len);
     n = ((L + kPage - 1) / kPage + per_wg - 1) / per_wg;
   }
-  if (n <= 1) return;  // written directly by the attention kernel
+  if (MODE == kDense && n <= 1) return;  // written directly by the attention kernel
   const int tid = threadIdx.x, c4 = tid % NQ, part = tid / NQ;
   const float* ml = part_ml + 2 * ((size_t)unit * slots_per_unit * G + h);
   const float4* po = reinterpret_cast<const float4*>(part_o + ((size_t)unit * slots_per_unit * G + h) * D) + c4;
@@ -171,6 +171,16 @@ AttnPlan plan_attention(int units, int max_items) {
   p.items_per_wave = ipw;
   p.wg_per_unit = std::max(1, (max_items + kAttnWaves * ipw - 1) / (kAttnWaves * ipw));
   return p;
+}
+
+hipError_t launch_combine(const AttnArgs& a, int slots, hipStream_t stream) {
+  if (a.d == 128)
+    hipLaunchKernelGGL((combine_kernel<128, kList>), dim3((unsigned)(a.batch * a.hq)), dim3(256), 0, stream, a.part_o,
+                       a.part_ml, a.seq_lens, a.out, a.hq, a.hkv, 1, slots, a.max_seq_len);
+  else
+    hipLaunchKernelGGL((combine_kernel<64, kList>), dim3((unsigned)(a.batch * a.hq)), dim3(256), 0, stream, a.part_o,
+                       a.part_ml, a.seq_lens, a.out, a.hq, a.hkv, 1, slots, a.max_seq_len);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(AttnMode mode, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {

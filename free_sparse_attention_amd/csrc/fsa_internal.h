@@ -147,13 +147,20 @@ hipError_t launch_validate(const uint16_t* q, const int32_t* page_table, const i
                            int max_seq_len, hipStream_t stream);
 
 // One decode step's selection launch: the top-k selection of every (sequence,
-// KV head) plus the attention over its prefix and window pages.
+// KV head) with the attention over the selected pages, plus the attention over
+// the prefix and window pages.
 struct StepArgs {
   const float* scores;        // [B][Hkv][max_pages] Quest scores
   const int32_t* page_table;  // [B][max_pages]
   const int32_t* seq_lens;    // [B]
   int32_t* sel_pages;         // [B][Hkv][budget] or null
-  int32_t* sel_work;          // [B][Hkv][sel_items][4]: selected items, then empty ones
+  // wide plan (sel_rep > 0): sel_rep workgroups per unit each select and attend
+  // items [r per, (r + 1) per) of the unit's list (selected, prefix, window)
+  int sel_rep, per;
+  // narrow plan (sel_rep == 0): one selection workgroup per unit writes the
+  // selected items to sel_work ([B][Hkv][sel_items][4]); pw_wg further
+  // workgroups per unit attend the prefix and window pages
+  int32_t* sel_work;
   int sel_items;
   int batch, hq, hkv, d, max_pages, prefix, window, budget, max_seq_len;
   const uint16_t* q;
@@ -161,7 +168,7 @@ struct StepArgs {
   const uint16_t* vc;
   float* part_o;       // partial slots [B][Hkv][slots_per_unit][G][D]
   float* part_ml;      // [B][Hkv][slots_per_unit][G][2]
-  int slots_per_unit;  // the prefix/window workgroups take slots [0, pw_wg)
+  int slots_per_unit;  // wide: slot r per replica; narrow: prefix/window workgroups first
   int pw_ipw;          // prefix/window items per wave
   int pw_wg;           // prefix/window workgroups per unit
   float scale_log2;
@@ -172,7 +179,17 @@ struct StepArgs {
 struct PwPlan {
   int max_items, ipw, wg_per_unit;
 };
-PwPlan plan_prefix_window(int units, int prefix, int window, int max_seq_len);
+PwPlan plan_prefix_window(int units, int busy_cus, int prefix, int window, int max_seq_len);
+
+// Plan of the step's selection launch: wide (sel_rep > 0) when one
+// selection replica per CU leaves at most 2 items per wave; otherwise
+// narrow, followed by the split-K attention over sel_items selected items.
+constexpr int kSliceMax = 256;  // selected items one replica can take
+struct StepPlan {
+  int sel_rep, per, sel_items;
+  PwPlan pw;
+};
+StepPlan plan_step(int units, int prefix, int window, int budget, int max_seq_len);
 hipError_t launch_select_attend(const StepArgs& a, hipStream_t stream);
 
 // Attention work-item sources: every page of the sequence, or the selection's work list.
@@ -202,5 +219,8 @@ AttnPlan plan_attention(int units, int max_items);
 // Split-K attention over the unit's items, then (when a unit can need more
 // than one workgroup) the combine of its partials.
 hipError_t launch_attention(AttnMode mode, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
+
+// Merge of all `slots` partials of every unit into the output (decode step).
+hipError_t launch_combine(const AttnArgs& a, int slots, hipStream_t stream);
 
 }  // namespace fsa

@@ -75,6 +75,8 @@ struct SelectJob {
   int32_t* counts;  // the unit's (k, items), or null
   int32_t* sel_work;  // or null: the selected items alone, (page, pool page, lo, hi) at [o],
   int sel_items;      // padded with empty items up to sel_items
+  int4* slice;        // or null: selected items [slice_lo, slice_lo + slice_cap) go to
+  int slice_lo, slice_cap;  // slice[o - slice_lo] (typically LDS)
 };
 
 __device__ __forceinline__ void put_item(int32_t* work, int idx, int p, int phys, int lo, int hi) {
@@ -106,8 +108,15 @@ __device__ __forceinline__ uint32_t wave_word_prefix(const uint32_t* cnt, int nw
 
 // COLS: pages per thread, a power of two with 1024 COLS >= ceil(max_seq_len / 16)
 // (a compile-time trip count: the per-page loops carry no guards).
+// What the selection leaves its caller: k, the number of selected pages, and
+// L, the sequence length (clamped to the host bound).
+struct SelectResult {
+  int k, L;
+};
+
+// After the call, S.sphys[p] holds page_table[b][p] for p < n_max.
 template <int COLS>
-__device__ __forceinline__ void select_unit(SelectLds& S, const SelectJob& J) {
+__device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJob& J) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n_max = (J.max_seq_len + kPage - 1) / kPage;  // pages any sequence can have
@@ -279,8 +288,10 @@ __device__ __forceinline__ void select_unit(SelectLds& S, const SelectJob& J) {
       const int p = tid + kSelThreads * j;
       const int o = base + (int)lanes_below(g);
       if (J.sel) J.sel[o] = p;
-      if (selw)
-        put_item(selw, o, p, S.sphys[p], max(p * kPage, Pe) - p * kPage, min(p * kPage + kPage, Ws) - p * kPage);
+      const int lo = max(p * kPage, Pe) - p * kPage, hi = min(p * kPage + kPage, Ws) - p * kPage;
+      if (selw) put_item(selw, o, p, S.sphys[p], lo, hi);
+      if (J.slice && (unsigned)(o - J.slice_lo) < (unsigned)J.slice_cap)
+        J.slice[o - J.slice_lo] = make_int4(p, S.sphys[p], lo, hi);
     }
   }
   // Stores come last: on this target every load wait also waits for earlier stores.
@@ -301,6 +312,7 @@ __device__ __forceinline__ void select_unit(SelectLds& S, const SelectJob& J) {
                min(p * kPage + kPage, L) - p * kPage);
     }
   }
+  return SelectResult{k, L};
 }
 
 }  // namespace fsa

@@ -47,47 +47,49 @@ __global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
   select_unit<COLS>(S, J);
 }
 
-// Attention over the prefix and window pages of one unit: pages [0, n_pre)
-// and [w_first, ceil(L / 16)), item i of the unit's list being prefix page i
-// for i < n_pre, else window page w_first + i - n_pre.  Wave w of workgroup wg
-// takes items (16 wg + w) ipw + [0, ipw).
+// Item i of a unit's prefix/window list for a sequence of length L: prefix
+// page i for i < n_pre, else window page w_first + i - n_pre.  Returns false
+// (and an empty range) past the end.
+__device__ __forceinline__ bool prefix_window_item(int i, int L, int prefix, int window, int& p, int& lo, int& hi) {
+  const int Pe = min(prefix, L), Ws = max(0, L - window);
+  const int n_pre = (Pe + kPage - 1) / kPage;
+  const int w0 = max(Ws, Pe);
+  const int w_first = w0 / kPage, n_pages = (L + kPage - 1) / kPage;
+  const int n_win = (L > w0) ? n_pages - w_first : 0;
+  p = 0;
+  lo = hi = 0;
+  if (i < 0 || i >= n_pre + n_win) return false;
+  if (i < n_pre) {
+    p = i;
+    hi = min(kPage, Pe - p * kPage);
+  } else {
+    p = w_first + i - n_pre;
+    lo = max(p * kPage, w0) - p * kPage;
+    hi = min(p * kPage + kPage, L) - p * kPage;
+  }
+  return true;
+}
+
+// Narrow plan, prefix/window role: attention over the prefix and window pages
+// of one unit.  Wave w of workgroup wg takes items (16 wg + w) ipw + [0, ipw).
 template <int D>
 __device__ __forceinline__ void prefix_window_attend(MergeLds<D, kSelWaves>& S, const StepArgs& A, int unit,
                                                      int wg) {
   const int b = unit / A.hkv, g = unit % A.hkv, G = A.hq / A.hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i = (wg * kSelWaves + wave) * A.pw_ipw + lane;
+  const int i = lane < A.pw_ipw ? (wg * kSelWaves + wave) * A.pw_ipw + lane : -1;
   const int32_t* pt = A.page_table + (size_t)b * A.max_pages;
-  // Item i of a sequence of length L: page, token range (lo, hi empty if none).
-  auto item = [&](int L, int& p, int& lo, int& hi) {
-    const int Pe = min(A.prefix, L), Ws = max(0, L - A.window);
-    const int n_pre = (Pe + kPage - 1) / kPage;
-    const int w0 = max(Ws, Pe);
-    const int w_first = w0 / kPage, n_pages = (L + kPage - 1) / kPage;
-    const int n_win = (L > w0) ? n_pages - w_first : 0;
-    p = 0;
-    lo = hi = 0;
-    if (lane >= A.pw_ipw || i >= n_pre + n_win) return;
-    if (i < n_pre) {
-      p = i;
-      hi = min(kPage, Pe - p * kPage);
-    } else {
-      p = w_first + i - n_pre;
-      lo = max(p * kPage, w0) - p * kPage;
-      hi = min(p * kPage + kPage, L) - p * kPage;
-    }
-  };
   // The page-table entry is loaded for the item the host-side length bound
   // implies, together with the length itself and q; it is loaded again only
   // where the actual length moves the item to another page.
   int p_guess, lo, hi;
-  item(A.max_seq_len, p_guess, lo, hi);
+  prefix_window_item(i, A.max_seq_len, A.prefix, A.window, p_guess, lo, hi);
   int my_phys = pt[p_guess];
   bf16x8_t qb[D / 32];
   load_q_operand<D>(A.q + ((size_t)b * A.hq + (size_t)g * G) * D, G, qb);
   const int L = min(A.seq_lens[b], A.max_seq_len);
   int p, my_lo, my_hi;
-  item(L, p, my_lo, my_hi);
+  prefix_window_item(i, L, A.prefix, A.window, p, my_lo, my_hi);
   if (my_lo < my_hi && p != p_guess) my_phys = pt[p];
   const int n = __popcll(__ballot(my_lo < my_hi));  // a prefix of the wave's lanes
   WaveAttn<D> st;
@@ -97,29 +99,87 @@ __device__ __forceinline__ void prefix_window_attend(MergeLds<D, kSelWaves>& S, 
   merge_waves<D, kSelWaves>(S, st, G, false, nullptr, A.part_o + slot * G * D, A.part_ml + 2 * slot * G);
 }
 
+__device__ __forceinline__ SelectJob step_job(const StepArgs& A, int unit) {
+  const int b = unit / A.hkv;
+  SelectJob J;
+  J.scores = A.scores + (size_t)unit * A.max_pages;
+  J.pt = A.page_table + (size_t)b * A.max_pages;
+  J.seq_len = A.seq_lens + b;
+  J.minmax = nullptr;
+  J.max_seq_len = A.max_seq_len;
+  J.prefix = A.prefix;
+  J.window = A.window;
+  J.budget = A.budget;
+  J.max_items = 0;
+  J.work = nullptr;
+  J.sel = A.sel_pages ? A.sel_pages + (size_t)unit * A.budget : nullptr;
+  J.counts = nullptr;
+  J.sel_work = nullptr;
+  J.sel_items = 0;
+  J.slice = nullptr;
+  J.slice_lo = J.slice_cap = 0;
+  return J;
+}
+
+// Wide plan: the sel_rep workgroups of a unit each run the same selection
+// (deterministic, so they agree) and then attend their share of the unit's
+// item list -- the selected pages in output-slot order, then the prefix pages,
+// then the window pages: workgroup r takes items [r per, (r + 1) per).
+// Running the selection redundantly on otherwise idle CUs costs nothing on
+// the critical path and spares a launch and a round trip for a work list.
+template <int COLS, int D>
+__device__ __forceinline__ void select_and_attend(SelectLds& SL, MergeLds<D, kSelWaves>& SM, int4* slice,
+                                                  const StepArgs& A, int unit, int r) {
+  const int b = unit / A.hkv, g = unit % A.hkv, G = A.hq / A.hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  SelectJob J = step_job(A, unit);
+  if (r != 0) J.sel = nullptr;
+  J.slice = slice;
+  J.slice_lo = r * A.per;
+  J.slice_cap = A.per;
+  const SelectResult R = select_unit<COLS>(SL, J);
+  __syncthreads();  // the slice is complete
+  const int ipw = (A.per + kSelWaves - 1) / kSelWaves;
+  const int local = wave * ipw + lane;
+  const int i = r * A.per + local;
+  int my_phys = 0, my_lo = 0, my_hi = 0;
+  if (lane < ipw && local < A.per) {
+    if (i < R.k) {
+      const int4 it = slice[local];
+      my_phys = it.y;
+      my_lo = it.z;
+      my_hi = it.w;
+    } else {
+      int p;
+      if (prefix_window_item(i - R.k, R.L, A.prefix, A.window, p, my_lo, my_hi)) my_phys = SL.sphys[p];
+    }
+  }
+  __syncthreads();  // every read of the selection's LDS precedes the merge that reuses it
+  const int n = __popcll(__ballot(my_lo < my_hi));  // a prefix of the wave's lanes
+  bf16x8_t qb[D / 32];
+  load_q_operand<D>(A.q + ((size_t)b * A.hq + (size_t)g * G) * D, G, qb);
+  WaveAttn<D> st;
+  attend_items<D, false>(A.kc, A.vc, (size_t)g * (kPage * D), (size_t)A.hkv * (kPage * D), qb, my_phys, my_lo,
+                         my_hi, n, A.scale_log2, st);
+  const size_t slot = (size_t)unit * A.slots_per_unit + r;
+  merge_waves<D, kSelWaves>(SM, st, G, false, nullptr, A.part_o + slot * G * D, A.part_ml + 2 * slot * G);
+}
+
 template <int COLS, int D>
 __global__ __launch_bounds__(kSelThreads) void select_attend_kernel(const StepArgs A) {
   __shared__ union {
     SelectLds sel;
     MergeLds<D, kSelWaves> att;
   } U;
+  __shared__ int4 slice[kSliceMax];
   const int units = A.batch * A.hkv;
-  if ((int)blockIdx.x < units) {
-    const int unit = blockIdx.x, b = unit / A.hkv;
-    SelectJob J;
-    J.scores = A.scores + (size_t)unit * A.max_pages;
-    J.pt = A.page_table + (size_t)b * A.max_pages;
-    J.seq_len = A.seq_lens + b;
-    J.minmax = nullptr;
-    J.max_seq_len = A.max_seq_len;
-    J.prefix = A.prefix;
-    J.window = A.window;
-    J.budget = A.budget;
-    J.max_items = 0;
-    J.work = nullptr;
-    J.sel = A.sel_pages ? A.sel_pages + (size_t)unit * A.budget : nullptr;
-    J.counts = nullptr;
-    J.sel_work = A.sel_work + 4 * (size_t)unit * A.sel_items;
+  if (A.sel_rep > 0) {
+    select_and_attend<COLS, D>(U.sel, U.att, slice, A, blockIdx.x / A.sel_rep, blockIdx.x % A.sel_rep);
+  } else if ((int)blockIdx.x < units) {
+    // narrow plan, selection role: the selected items go to the work list of
+    // the split-K attention kernel
+    SelectJob J = step_job(A, blockIdx.x);
+    J.sel_work = A.sel_work + 4 * (size_t)blockIdx.x * A.sel_items;
     J.sel_items = A.sel_items;
     select_unit<COLS>(U.sel, J);
   } else {
@@ -153,7 +213,7 @@ hipError_t launch_select_pages(const float* scores, const int32_t* page_table,
   return hipGetLastError();
 }
 
-PwPlan plan_prefix_window(int units, int prefix, int window, int max_seq_len) {
+PwPlan plan_prefix_window(int units, int busy_cus, int prefix, int window, int max_seq_len) {
   const int n_max = (max_seq_len + kPage - 1) / kPage;
   const int pre = std::min((prefix + kPage - 1) / kPage, n_max);
   const int win = std::min((window + kPage - 1) / kPage + 1, n_max);
@@ -164,16 +224,44 @@ PwPlan plan_prefix_window(int units, int prefix, int window, int max_seq_len) {
     p.wg_per_unit = 0;
     return p;
   }
-  // one workgroup per CU (the launch's LDS), the CUs beside the selection's
-  const long waves = (long)std::max(1, device_cu_count() - units) * kSelWaves;
+  // one workgroup per CU (the launch's LDS), on the CUs beside the selection's
+  const long waves = (long)std::max(1, device_cu_count() - busy_cus) * kSelWaves;
   const long need = (long)units * p.max_items;
   p.ipw = (int)std::max<long>(1, std::min<long>(kWave, (need + waves - 1) / waves));
   p.wg_per_unit = (p.max_items + kSelWaves * p.ipw - 1) / (kSelWaves * p.ipw);
   return p;
 }
 
+StepPlan plan_step(int units, int prefix, int window, int budget, int max_seq_len) {
+  const int n_max = (max_seq_len + kPage - 1) / kPage;
+  const int pre = std::min((prefix + kPage - 1) / kPage, n_max);
+  const int win = std::min((window + kPage - 1) / kPage + 1, n_max);
+  StepPlan p;
+  p.sel_items = std::max(1, std::min(budget, n_max));
+  // wide: one selection replica per CU, each attending at most 2 items per wave
+  // (one page at a time: a two-stage pipeline does not fit beside the
+  // selection in 128 registers, and a third page costs more than the
+  // narrow plan's extra launch)
+  const int rep = device_cu_count() / std::max(1, units);
+  const int items = p.sel_items + pre + win;
+  if (rep >= 1) {
+    const int per = (items + rep - 1) / rep;
+    if (per <= 2 * kSelWaves && per <= kSliceMax) {
+      p.sel_rep = rep;
+      p.per = per;
+      p.pw = PwPlan{0, 1, 0};
+      return p;
+    }
+  }
+  p.sel_rep = 0;
+  p.per = 0;
+  p.pw = plan_prefix_window(units, units, prefix, window, max_seq_len);
+  return p;
+}
+
 hipError_t launch_select_attend(const StepArgs& a, hipStream_t stream) {
-  const unsigned grid = (unsigned)(a.batch * a.hkv * (1 + a.pw_wg));
+  const unsigned grid =
+      (unsigned)(a.batch * a.hkv * (a.sel_rep > 0 ? a.sel_rep : 1 + a.pw_wg));
 #define FSA_SA(C, DD) hipLaunchKernelGGL((select_attend_kernel<C, DD>), dim3(grid), dim3(kSelThreads), 0, stream, a)
 #define FSA_SA_D(C)         \
   do {                      \
