@@ -33,6 +33,8 @@ template <int D, int WAVES>
 struct MergeLds {
   float o[WAVES][D][17];
   float m[WAVES][16], l[WAVES][16];
+  float e[WAVES][16];     // weight 2^(m_w - M) of wave w for head h
+  float M[16], L[16];     // per head: maximum and weighted sum
 };
 
 // B operand of QK for head column col of the group: q[col][32 ks + 8 gq .. +8],
@@ -166,26 +168,37 @@ __device__ __forceinline__ void merge_waves(MergeLds<D, WAVES>& S, const WaveAtt
 #pragma unroll
     for (int r = 0; r < 4; ++r) S.o[wave][16 * t + 4 * gq + r][col] = st.acc[t][r];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += WAVES * kWave) {
-    const int h = idx / D, d = idx % D;
+  // per head: the maximum, the waves' weights and the weighted sum, once
+  if (threadIdx.x < 16) {
+    const int h = threadIdx.x;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) M = fmaxf(M, S.m[w][h]);
-    float o = 0.f, l = 0.f;
+    float l = 0.f;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) {
       const float mw = S.m[w][h];
       const float e = mw == -INFINITY ? 0.f : exp2f(mw - M);
-      o += e * S.o[w][d][h];
+      S.e[w][h] = e;
       l += e * S.l[w][h];
     }
+    S.M[h] = M;
+    S.L[h] = l;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += WAVES * kWave) {
+    const int h = idx / D, d = idx % D;
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) o += S.e[w][h] * S.o[w][d][h];
     if (direct) {
+      const float l = S.L[h];
       out_rows[idx] = (uint16_t)f32_to_bf16_bits(l > 0.f ? o / l : 0.f);
     } else {
       po[idx] = o;
       if (d == 0) {
-        pml[2 * h] = M;
-        pml[2 * h + 1] = l;
+        pml[2 * h] = S.M[h];
+        pml[2 * h + 1] = S.L[h];
       }
     }
   }

@@ -76,7 +76,8 @@ struct SelectJob {
   int32_t* sel_work;  // or null: the selected items alone, (page, pool page, lo, hi) at [o],
   int sel_items;      // padded with empty items up to sel_items
   int4* slice;        // or null: selected items [slice_lo, slice_lo + slice_cap) go to
-  int slice_lo, slice_cap;  // slice[o - slice_lo] (typically LDS)
+  int slice_lo, slice_cap;  // slice[o - slice_lo] (typically LDS); with slice_after_pw,
+  bool slice_after_pw;      // slice_lo counts in a list of prefix and window pages, then selected ones
 };
 
 __device__ __forceinline__ void put_item(int32_t* work, int idx, int p, int phys, int lo, int hi) {
@@ -277,6 +278,7 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
   __syncthreads();
   const uint32_t P = wave_word_prefix(S.cnt[1], nwords, wave, lane);
   int32_t* selw = J.sel_work ? J.sel_work : (J.work ? J.work + 4 * n_pre : nullptr);  // item o of the selection
+  const int slice_lo = J.slice_after_pw ? J.slice_lo - (n_pre + n_win) : J.slice_lo;
 #pragma unroll
   for (int j = 0; j < COLS; ++j) {
     const bool t = (mine >> j) & 1u;
@@ -290,8 +292,8 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
       if (J.sel) J.sel[o] = p;
       const int lo = max(p * kPage, Pe) - p * kPage, hi = min(p * kPage + kPage, Ws) - p * kPage;
       if (selw) put_item(selw, o, p, S.sphys[p], lo, hi);
-      if (J.slice && (unsigned)(o - J.slice_lo) < (unsigned)J.slice_cap)
-        J.slice[o - J.slice_lo] = make_int4(p, S.sphys[p], lo, hi);
+      if (J.slice && (unsigned)(o - slice_lo) < (unsigned)J.slice_cap)
+        J.slice[o - slice_lo] = make_int4(p, S.sphys[p], lo, hi);
     }
   }
   // Stores come last: on this target every load wait also waits for earlier stores.

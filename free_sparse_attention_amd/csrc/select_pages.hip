@@ -47,6 +47,14 @@ __global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
   select_unit<COLS>(S, J);
 }
 
+// Prefix and window pages of a sequence of length L.
+__device__ __forceinline__ int prefix_window_count(int L, int prefix, int window) {
+  const int Pe = min(prefix, L), Ws = max(0, L - window);
+  const int w0 = max(Ws, Pe);
+  const int n_win = (L > w0) ? (L + kPage - 1) / kPage - w0 / kPage : 0;
+  return (Pe + kPage - 1) / kPage + n_win;
+}
+
 // Item i of a unit's prefix/window list for a sequence of length L: prefix
 // page i for i < n_pre, else window page w_first + i - n_pre.  Returns false
 // (and an empty range) past the end.
@@ -118,43 +126,71 @@ __device__ __forceinline__ SelectJob step_job(const StepArgs& A, int unit) {
   J.sel_items = 0;
   J.slice = nullptr;
   J.slice_lo = J.slice_cap = 0;
+  J.slice_after_pw = false;
   return J;
 }
 
-// Wide plan: the sel_rep workgroups of a unit each run the same selection
-// (deterministic, so they agree) and then attend their share of the unit's
-// item list -- the selected pages in output-slot order, then the prefix pages,
-// then the window pages: workgroup r takes items [r per, (r + 1) per).
-// Running the selection redundantly on otherwise idle CUs costs nothing on
-// the critical path and spares a launch and a round trip for a work list.
+// Wide plan: the sel_rep workgroups of a unit share out the unit's item list
+// -- its prefix pages, its window pages, then its selected pages in output-slot
+// order -- workgroup r taking items [r per, (r + 1) per).  A workgroup whose
+// items are all prefix or window pages attends them at once, its loads
+// overlapping the selection of the others; every other workgroup runs the
+// unit's selection (deterministic, so the replicas agree) and then attends its
+// share.  Running the selection redundantly on otherwise idle CUs costs
+// nothing on the critical path and spares a launch and a round trip for a work
+// list.  Whether a workgroup needs the selection is decided from the host-side
+// length bound; a shorter sequence only moves work between the two kinds.
 template <int COLS, int D>
 __device__ __forceinline__ void select_and_attend(SelectLds& SL, MergeLds<D, kSelWaves>& SM, int4* slice,
                                                   const StepArgs& A, int unit, int r) {
   const int b = unit / A.hkv, g = unit % A.hkv, G = A.hq / A.hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  SelectJob J = step_job(A, unit);
-  if (r != 0) J.sel = nullptr;
-  J.slice = slice;
-  J.slice_lo = r * A.per;
-  J.slice_cap = A.per;
-  const SelectResult R = select_unit<COLS>(SL, J);
-  __syncthreads();  // the slice is complete
   const int ipw = (A.per + kSelWaves - 1) / kSelWaves;
   const int local = wave * ipw + lane;
-  const int i = r * A.per + local;
+  const int i = (lane < ipw && local < A.per) ? r * A.per + local : -1;
+  const int32_t* pt = A.page_table + (size_t)b * A.max_pages;
   int my_phys = 0, my_lo = 0, my_hi = 0;
-  if (lane < ipw && local < A.per) {
-    if (i < R.k) {
-      const int4 it = slice[local];
-      my_phys = it.y;
-      my_lo = it.z;
-      my_hi = it.w;
-    } else {
-      int p;
-      if (prefix_window_item(i - R.k, R.L, A.prefix, A.window, p, my_lo, my_hi)) my_phys = SL.sphys[p];
+  int p, lo, hi;
+  const int n_pw_h = prefix_window_count(A.max_seq_len, A.prefix, A.window);
+  bool done = false;
+  if ((r + 1) * A.per <= n_pw_h) {
+    // prefix/window items only (by the host bound): page-table entries are
+    // loaded for the bound's items together with the length
+    int p_guess;
+    prefix_window_item(i, A.max_seq_len, A.prefix, A.window, p_guess, lo, hi);
+    my_phys = pt[p_guess];
+    const int L = min(A.seq_lens[b], A.max_seq_len);
+    if ((r + 1) * A.per <= prefix_window_count(L, A.prefix, A.window)) {
+      prefix_window_item(i, L, A.prefix, A.window, p, my_lo, my_hi);
+      if (my_lo < my_hi && p != p_guess) my_phys = pt[p];
+      done = true;
     }
   }
-  __syncthreads();  // every read of the selection's LDS precedes the merge that reuses it
+  if (!done) {
+    SelectJob J = step_job(A, unit);
+    // the last replica always selects (its items reach past every prefix and
+    // window page): it reports the selected pages
+    if (r != A.sel_rep - 1) J.sel = nullptr;
+    J.slice = slice;
+    J.slice_lo = r * A.per;
+    J.slice_cap = A.per;
+    J.slice_after_pw = true;
+    const SelectResult R = select_unit<COLS>(SL, J);
+    __syncthreads();  // the slice is complete
+    my_phys = my_lo = my_hi = 0;
+    const int n_pw = prefix_window_count(R.L, A.prefix, A.window);
+    if (i >= 0 && i < n_pw + R.k) {
+      if (i >= n_pw) {
+        const int4 it = slice[local];
+        my_phys = it.y;
+        my_lo = it.z;
+        my_hi = it.w;
+      } else if (prefix_window_item(i, R.L, A.prefix, A.window, p, my_lo, my_hi)) {
+        my_phys = SL.sphys[p];
+      }
+    }
+    __syncthreads();  // every read of the selection's LDS precedes the merge that reuses it
+  }
   const int n = __popcll(__ballot(my_lo < my_hi));  // a prefix of the wave's lanes
   bf16x8_t qb[D / 32];
   load_q_operand<D>(A.q + ((size_t)b * A.hq + (size_t)g * G) * D, G, qb);
