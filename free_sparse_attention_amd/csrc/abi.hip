@@ -99,9 +99,9 @@ int candidate_pages(fsa_layer_cfg c, int32_t L) {
 }
 
 // Workspace of the sparse step: [scores][selected items (narrow plan)]
-// [part_ml][part_o].  Partial slots per unit: wide plan, one per selection
-// replica; narrow plan, the prefix/window workgroups first, then the split-K
-// workgroups over the selected items.  When no sequence can have more
+// [part_ml][part_o].  Partial slots per unit: the prefix/window workgroups
+// first, then one per selection replica (wide plan) or the split-K workgroups
+// over the selected items (narrow plan).  When no sequence can have more
 // candidate pages than the budget, every candidate is taken, the attended set
 // is the whole sequence and the step runs the dense kernels (dense plan).
 struct SparseWs {
@@ -128,7 +128,7 @@ SparseWs sparse_ws(const fsa_dims* d, fsa_layer_cfg c, int32_t max_seq_len) {
     w.step = fsa::plan_step(units, c.prefix_tokens, c.window_tokens, c.budget_pages, max_seq_len);
     if (w.step.sel_rep > 0) {
       w.plan = fsa::AttnPlan{0, 0};
-      w.slots = w.step.sel_rep;
+      w.slots = w.step.pw.wg_per_unit + w.step.sel_rep;
     } else {
       w.plan = fsa::plan_attention(units, w.step.sel_items);
       w.slots = w.step.pw.wg_per_unit + w.plan.wg_per_unit;

@@ -155,20 +155,20 @@ struct StepArgs {
   const int32_t* seq_lens;    // [B]
   int32_t* sel_pages;         // [B][Hkv][budget] or null
   // wide plan (sel_rep > 0): sel_rep workgroups per unit each select and attend
-  // items [r per, (r + 1) per) of the unit's list (selected, prefix, window)
+  // selected items [r per, (r + 1) per)
   int sel_rep, per;
   // narrow plan (sel_rep == 0): one selection workgroup per unit writes the
-  // selected items to sel_work ([B][Hkv][sel_items][4]); pw_wg further
-  // workgroups per unit attend the prefix and window pages
+  // selected items to sel_work ([B][Hkv][sel_items][4]) for the split-K kernel
   int32_t* sel_work;
   int sel_items;
+  // both plans: pw_wg further workgroups per unit attend the prefix and window pages
   int batch, hq, hkv, d, max_pages, prefix, window, budget, max_seq_len;
   const uint16_t* q;
   const uint16_t* kc;
   const uint16_t* vc;
   float* part_o;       // partial slots [B][Hkv][slots_per_unit][G][D]
   float* part_ml;      // [B][Hkv][slots_per_unit][G][2]
-  int slots_per_unit;  // wide: slot r per replica; narrow: prefix/window workgroups first
+  int slots_per_unit;  // prefix/window workgroups first, then the selection replicas (wide)
   int pw_ipw;          // prefix/window items per wave
   int pw_wg;           // prefix/window workgroups per unit
   float scale_log2;
@@ -181,9 +181,9 @@ struct PwPlan {
 };
 PwPlan plan_prefix_window(int units, int busy_cus, int prefix, int window, int max_seq_len);
 
-// Plan of the step's selection launch: wide (sel_rep > 0) when one
-// selection replica per CU leaves at most 2 items per wave; otherwise
-// narrow, followed by the split-K attention over sel_items selected items.
+// Plan of the step's selection launch: wide (sel_rep > 0) when selection
+// replicas with at most 2 selected pages per wave fit on half the CUs;
+// otherwise narrow, followed by the split-K attention over sel_items items.
 constexpr int kSliceMax = 256;  // selected items one replica can take
 struct StepPlan {
   int sel_rep, per, sel_items;

@@ -76,8 +76,7 @@ struct SelectJob {
   int32_t* sel_work;  // or null: the selected items alone, (page, pool page, lo, hi) at [o],
   int sel_items;      // padded with empty items up to sel_items
   int4* slice;        // or null: selected items [slice_lo, slice_lo + slice_cap) go to
-  int slice_lo, slice_cap;  // slice[o - slice_lo] (typically LDS); with slice_after_pw,
-  bool slice_after_pw;      // slice_lo counts in a list of prefix and window pages, then selected ones
+  int slice_lo, slice_cap;  // slice[o - slice_lo] (typically LDS)
 };
 
 __device__ __forceinline__ void put_item(int32_t* work, int idx, int p, int phys, int lo, int hi) {
@@ -278,7 +277,7 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
   __syncthreads();
   const uint32_t P = wave_word_prefix(S.cnt[1], nwords, wave, lane);
   int32_t* selw = J.sel_work ? J.sel_work : (J.work ? J.work + 4 * n_pre : nullptr);  // item o of the selection
-  const int slice_lo = J.slice_after_pw ? J.slice_lo - (n_pre + n_win) : J.slice_lo;
+  const int slice_lo = J.slice_lo;
 #pragma unroll
   for (int j = 0; j < COLS; ++j) {
     const bool t = (mine >> j) & 1u;

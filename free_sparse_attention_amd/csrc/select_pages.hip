@@ -47,14 +47,6 @@ __global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
   select_unit<COLS>(S, J);
 }
 
-// Prefix and window pages of a sequence of length L.
-__device__ __forceinline__ int prefix_window_count(int L, int prefix, int window) {
-  const int Pe = min(prefix, L), Ws = max(0, L - window);
-  const int w0 = max(Ws, Pe);
-  const int n_win = (L > w0) ? (L + kPage - 1) / kPage - w0 / kPage : 0;
-  return (Pe + kPage - 1) / kPage + n_win;
-}
-
 // Item i of a unit's prefix/window list for a sequence of length L: prefix
 // page i for i < n_pre, else window page w_first + i - n_pre.  Returns false
 // (and an empty range) past the end.
@@ -126,81 +118,50 @@ __device__ __forceinline__ SelectJob step_job(const StepArgs& A, int unit) {
   J.sel_items = 0;
   J.slice = nullptr;
   J.slice_lo = J.slice_cap = 0;
-  J.slice_after_pw = false;
   return J;
 }
 
-// Wide plan: the sel_rep workgroups of a unit share out the unit's item list
-// -- its prefix pages, its window pages, then its selected pages in output-slot
-// order -- workgroup r taking items [r per, (r + 1) per).  A workgroup whose
-// items are all prefix or window pages attends them at once, its loads
-// overlapping the selection of the others; every other workgroup runs the
-// unit's selection (deterministic, so the replicas agree) and then attends its
-// share.  Running the selection redundantly on otherwise idle CUs costs
-// nothing on the critical path and spares a launch and a round trip for a work
-// list.  Whether a workgroup needs the selection is decided from the host-side
-// length bound; a shorter sequence only moves work between the two kinds.
+// Wide plan, selection role: the sel_rep workgroups of a unit each run the
+// unit's selection (deterministic, so the replicas agree) and then attend
+// their own slice of the selected pages, in output-slot order: replica r takes
+// selected items [r per, (r + 1) per), at most two per wave.  Running the
+// selection redundantly on otherwise idle CUs costs nothing on the critical
+// path and spares a launch and a round trip for a work list.
 template <int COLS, int D>
 __device__ __forceinline__ void select_and_attend(SelectLds& SL, MergeLds<D, kSelWaves>& SM, int4* slice,
                                                   const StepArgs& A, int unit, int r) {
   const int b = unit / A.hkv, g = unit % A.hkv, G = A.hq / A.hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  SelectJob J = step_job(A, unit);
+  if (r != 0) J.sel = nullptr;
+  J.slice = slice;
+  J.slice_lo = r * A.per;
+  J.slice_cap = A.per;
+  const SelectResult R = select_unit<COLS>(SL, J);
+  __syncthreads();  // the slice is complete
   const int ipw = (A.per + kSelWaves - 1) / kSelWaves;
   const int local = wave * ipw + lane;
-  const int i = (lane < ipw && local < A.per) ? r * A.per + local : -1;
-  const int32_t* pt = A.page_table + (size_t)b * A.max_pages;
   int my_phys = 0, my_lo = 0, my_hi = 0;
-  int p, lo, hi;
-  const int n_pw_h = prefix_window_count(A.max_seq_len, A.prefix, A.window);
-  bool done = false;
-  if ((r + 1) * A.per <= n_pw_h) {
-    // prefix/window items only (by the host bound): page-table entries are
-    // loaded for the bound's items together with the length
-    int p_guess;
-    prefix_window_item(i, A.max_seq_len, A.prefix, A.window, p_guess, lo, hi);
-    my_phys = pt[p_guess];
-    const int L = min(A.seq_lens[b], A.max_seq_len);
-    if ((r + 1) * A.per <= prefix_window_count(L, A.prefix, A.window)) {
-      prefix_window_item(i, L, A.prefix, A.window, p, my_lo, my_hi);
-      if (my_lo < my_hi && p != p_guess) my_phys = pt[p];
-      done = true;
-    }
+  if (lane < ipw && local < A.per && r * A.per + local < R.k) {
+    const int4 it = slice[local];
+    my_phys = it.y;
+    my_lo = it.z;
+    my_hi = it.w;
   }
-  if (!done) {
-    SelectJob J = step_job(A, unit);
-    // the last replica always selects (its items reach past every prefix and
-    // window page): it reports the selected pages
-    if (r != A.sel_rep - 1) J.sel = nullptr;
-    J.slice = slice;
-    J.slice_lo = r * A.per;
-    J.slice_cap = A.per;
-    J.slice_after_pw = true;
-    const SelectResult R = select_unit<COLS>(SL, J);
-    __syncthreads();  // the slice is complete
-    my_phys = my_lo = my_hi = 0;
-    const int n_pw = prefix_window_count(R.L, A.prefix, A.window);
-    if (i >= 0 && i < n_pw + R.k) {
-      if (i >= n_pw) {
-        const int4 it = slice[local];
-        my_phys = it.y;
-        my_lo = it.z;
-        my_hi = it.w;
-      } else if (prefix_window_item(i, R.L, A.prefix, A.window, p, my_lo, my_hi)) {
-        my_phys = SL.sphys[p];
-      }
-    }
-    __syncthreads();  // every read of the selection's LDS precedes the merge that reuses it
-  }
+  __syncthreads();  // every read of the selection's LDS precedes the merge that reuses it
   const int n = __popcll(__ballot(my_lo < my_hi));  // a prefix of the wave's lanes
   bf16x8_t qb[D / 32];
   load_q_operand<D>(A.q + ((size_t)b * A.hq + (size_t)g * G) * D, G, qb);
   WaveAttn<D> st;
   attend_items<D, false>(A.kc, A.vc, (size_t)g * (kPage * D), (size_t)A.hkv * (kPage * D), qb, my_phys, my_lo,
                          my_hi, n, A.scale_log2, st);
-  const size_t slot = (size_t)unit * A.slots_per_unit + r;
+  const size_t slot = (size_t)unit * A.slots_per_unit + A.pw_wg + r;
   merge_waves<D, kSelWaves>(SM, st, G, false, nullptr, A.part_o + slot * G * D, A.part_ml + 2 * slot * G);
 }
 
+// Workgroups, in launch order: the selection workgroups (sel_rep per unit in
+// the wide plan, one per unit in the narrow plan), then pw_wg prefix/window
+// workgroups per unit.
 template <int COLS, int D>
 __global__ __launch_bounds__(kSelThreads) void select_attend_kernel(const StepArgs A) {
   __shared__ union {
@@ -209,17 +170,20 @@ __global__ __launch_bounds__(kSelThreads) void select_attend_kernel(const StepAr
   } U;
   __shared__ int4 slice[kSliceMax];
   const int units = A.batch * A.hkv;
-  if (A.sel_rep > 0) {
-    select_and_attend<COLS, D>(U.sel, U.att, slice, A, blockIdx.x / A.sel_rep, blockIdx.x % A.sel_rep);
-  } else if ((int)blockIdx.x < units) {
-    // narrow plan, selection role: the selected items go to the work list of
-    // the split-K attention kernel
-    SelectJob J = step_job(A, blockIdx.x);
-    J.sel_work = A.sel_work + 4 * (size_t)blockIdx.x * A.sel_items;
-    J.sel_items = A.sel_items;
-    select_unit<COLS>(U.sel, J);
+  const int n_sel = units * (A.sel_rep > 0 ? A.sel_rep : 1);
+  if ((int)blockIdx.x < n_sel) {
+    if (A.sel_rep > 0) {
+      select_and_attend<COLS, D>(U.sel, U.att, slice, A, blockIdx.x / A.sel_rep, blockIdx.x % A.sel_rep);
+    } else {
+      // narrow plan: the selected items go to the work list of the split-K
+      // attention kernel
+      SelectJob J = step_job(A, blockIdx.x);
+      J.sel_work = A.sel_work + 4 * (size_t)blockIdx.x * A.sel_items;
+      J.sel_items = A.sel_items;
+      select_unit<COLS>(U.sel, J);
+    }
   } else {
-    const int w = blockIdx.x - units;
+    const int w = blockIdx.x - n_sel;
     prefix_window_attend<D>(U.att, A, w / A.pw_wg, w % A.pw_wg);
   }
 }
@@ -270,34 +234,30 @@ PwPlan plan_prefix_window(int units, int busy_cus, int prefix, int window, int m
 
 StepPlan plan_step(int units, int prefix, int window, int budget, int max_seq_len) {
   const int n_max = (max_seq_len + kPage - 1) / kPage;
-  const int pre = std::min((prefix + kPage - 1) / kPage, n_max);
-  const int win = std::min((window + kPage - 1) / kPage + 1, n_max);
+  const int cus = device_cu_count();
   StepPlan p;
   p.sel_items = std::max(1, std::min(budget, n_max));
-  // wide: one selection replica per CU, each attending at most 2 items per wave
-  // (one page at a time: a two-stage pipeline does not fit beside the
-  // selection in 128 registers, and a third page costs more than the
-  // narrow plan's extra launch)
-  const int rep = device_cu_count() / std::max(1, units);
-  const int items = p.sel_items + pre + win;
-  if (rep >= 1) {
-    const int per = (items + rep - 1) / rep;
-    if (per <= 2 * kSelWaves && per <= kSliceMax) {
-      p.sel_rep = rep;
-      p.per = per;
-      p.pw = PwPlan{0, 1, 0};
-      return p;
-    }
-  }
+  // Wide when the selection replicas fit on half the CUs with one, else two,
+  // selected pages per wave (one page at a time: a two-stage pipeline does not
+  // fit beside the selection in 128 registers); the prefix/window workgroups
+  // take the other CUs.
   p.sel_rep = 0;
   p.per = 0;
-  p.pw = plan_prefix_window(units, units, prefix, window, max_seq_len);
+  for (int ipw = 1; ipw <= 2 && p.sel_rep == 0; ++ipw) {
+    const int per = ipw * kSelWaves;
+    const int rep = (p.sel_items + per - 1) / per;
+    if ((long)units * rep <= cus / 2) {
+      p.sel_rep = rep;
+      p.per = (p.sel_items + rep - 1) / rep;
+    }
+  }
+  const int busy = units * std::max(1, p.sel_rep);
+  p.pw = plan_prefix_window(units, busy, prefix, window, max_seq_len);
   return p;
 }
 
 hipError_t launch_select_attend(const StepArgs& a, hipStream_t stream) {
-  const unsigned grid =
-      (unsigned)(a.batch * a.hkv * (a.sel_rep > 0 ? a.sel_rep : 1 + a.pw_wg));
+  const unsigned grid = (unsigned)(a.batch * a.hkv * ((a.sel_rep > 0 ? a.sel_rep : 1) + a.pw_wg));
 #define FSA_SA(C, DD) hipLaunchKernelGGL((select_attend_kernel<C, DD>), dim3(grid), dim3(kSelThreads), 0, stream, a)
 #define FSA_SA_D(C)         \
   do {                      \
