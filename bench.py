@@ -204,6 +204,64 @@ def crossover_sweep(steps, warmup):
     return rows
 
 
+CALIB_LENS = (16384, 65536, 131072, 262144)
+CALIB_GROUPS = (4, 8)
+CALIB_CFGS = ((128, 1024, 64), (128, 1024, 256), (128, 1024, 1024), (128, 4096, 64), (128, 4096, 256),
+              (128, 4096, 1024))
+
+
+def calibrate(steps, warmup):
+    """Step times over a grid of context lengths, query-group sizes and layer
+    configurations (prefix, window, budget), batch 4, Hkv 4, D 128: the data
+    the per-layer decode-cost model is fitted to."""
+    import torch
+
+    import free_sparse_attention_amd as fsa
+    import synth
+    from tests.gpu_harness import DeviceWorkload
+
+    rows = []
+    for G in CALIB_GROUPS:
+        for L in CALIB_LENS:
+            wl = synth.make_workload("ctx64k", seq_lens=(L,) * 4, hq=4 * G)
+            base = DeviceWorkload(wl)
+            R = 3
+            reps = [(base.k_cache, base.v_cache, base.meta)] + [
+                (base.k_cache.clone(), base.v_cache.clone(), base.meta.clone()) for _ in range(R - 1)]
+            out = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.bfloat16, device="cuda")
+            stream = torch.cuda.current_stream()
+
+            def timed(fn, n, w):
+                for i in range(w):
+                    fn(i)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for i in range(n):
+                    fn(w + i)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                return 1000.0 * e0.elapsed_time(e1) / n
+
+            dws = base.dense_workspace()
+            dense_us = timed(lambda i: fsa.dense_decode_attn(base.dims, wl.sm_scale, L, base.q, reps[i % R][0],
+                                                             reps[i % R][1], base.page_table, base.seq_lens, out,
+                                                             dws, stream), max(10, steps // 4), 3)
+            for cfg in CALIB_CFGS:
+                c = fsa.cfg(*cfg)
+                ws = base.workspace(cfg=cfg)
+                us = timed(lambda i: fsa.sparse_decode_attn(base.dims, c, wl.sm_scale, L, base.q, reps[i % R][0],
+                                                            reps[i % R][1], reps[i % R][2], base.page_table,
+                                                            base.seq_lens, out, None, ws, stream), steps, warmup)
+                rows.append({"batch": 4, "q_heads": 4 * G, "kv_heads": 4, "head_dim": 128, "seq_len": L,
+                             "prefix": cfg[0], "window": cfg[1], "budget_pages": cfg[2], "sparse_us": us,
+                             "dense_us": dense_us})
+                log(f"[calibrate] G={G} L={L} cfg={cfg}: sparse {us:.1f} us, dense {dense_us:.1f} us")
+            del reps, base, wl
+            torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,6 +273,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="instead: sparse vs dense step time for context lengths 2k..256k")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="instead: step times over a grid of lengths, group sizes and layer configurations")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU; this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -224,6 +284,12 @@ def main():
     synth.lib()
     import free_sparse_attention_amd as fsa
     fsa.load()
+
+    if args.calibrate:
+        rows = calibrate(max(20, args.steps // 4), args.warmup)
+        print(json.dumps({"metric": "decode step time over layer configurations", "unit": "us", "n_gpus": 1,
+                          "data": "synthetic (seeded)", "rows": rows}), flush=True)
+        return
 
     if args.sweep:
         rows = crossover_sweep(max(20, args.steps // 4), args.warmup)

@@ -1,0 +1,124 @@
+"""Per-layer decode-cost model of the combined sparse attention step.
+
+The method's per-layer configuration search weighs the accuracy of a layer's
+(prefix, window, budget) choice against its estimated decoding cost (paper,
+analysis page "Methodology").  This module supplies that estimate for this
+library on MI355X: predicted microseconds of one ``fsa_sparse_decode_attn``
+call (and of the dense baseline) for given shapes and configuration, fitted
+by non-negative least squares to step times measured on the device
+(``bench.py --calibrate``, stored in ``cost_model_data.json``).
+
+Terms, per step (sums over the B x Hkv (sequence, KV head) units):
+
+* sparse, when some sequence has more candidate pages than the budget:
+  ``c0 + c_meta * metadata MB + c_cols * pages-per-thread of the selection
+  + c_ipw * selected pages per wave (wide plan) + c_narrow * [narrow plan]
+  + c_narrow_sel * selected K/V MB (narrow plan)``;
+* otherwise the step runs the dense kernels: the dense cost;
+* dense: ``d0 + d_kv * K/V MB``.
+
+The plan terms follow the library's launch planning: every candidate taken
+when C(L) <= budget; the wide plan when selection replicas with one (else
+two) selected pages per wave fit on half the CUs; else the narrow plan with
+a separate split-K launch.  The selection's pages per thread is the power of
+two that covers ceil(L / 16) pages with 1024 threads.
+"""
+from __future__ import annotations
+
+import json
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+PAGE = 16
+_DATA = os.path.join(os.path.dirname(os.path.abspath(__file__)), "cost_model_data.json")
+
+
+@dataclass(frozen=True)
+class StepShape:
+    batch: int
+    q_heads: int
+    kv_heads: int
+    head_dim: int
+    seq_len: int
+    prefix: int
+    window: int
+    budget_pages: int
+
+
+def _features(s: StepShape, compute_units: int) -> dict:
+    units = s.batch * s.kv_heads
+    n = -(-s.seq_len // PAGE)
+    pe, ws = min(s.prefix, s.seq_len), max(0, s.seq_len - s.window)
+    cand = (-(-ws // PAGE) - pe // PAGE) if pe < ws else 0
+    k = min(s.budget_pages, cand)
+    sel_items = max(1, min(s.budget_pages, n))
+    ipw_sel, narrow = 0, 1
+    for ipw in (1, 2):
+        rep = -(-sel_items // (16 * ipw))
+        if units * rep <= compute_units // 2:
+            ipw_sel, narrow = ipw, 0
+            break
+    cols = 1
+    while cols * 1024 < n:
+        cols *= 2
+    page_kv = 2 * PAGE * s.head_dim * 2  # K and V bytes of one page of one KV head
+    return {
+        "all_taken": cand <= s.budget_pages,
+        "meta_mb": units * cand * 4 * s.head_dim / 1e6,
+        "sel_mb": units * k * page_kv / 1e6,
+        "dense_mb": units * n * page_kv / 1e6,
+        "cols": cols, "ipw": ipw_sel, "narrow": narrow,
+    }
+
+
+def _sparse_row(f: dict) -> list:
+    return [1.0, f["meta_mb"], f["cols"], (1 - f["narrow"]) * f["ipw"], f["narrow"], f["narrow"] * f["sel_mb"]]
+
+
+SPARSE_TERMS = ("c0_us", "c_meta_us_per_mb", "c_cols_us", "c_ipw_us", "c_narrow_us", "c_narrow_sel_us_per_mb")
+DENSE_TERMS = ("d0_us", "d_kv_us_per_mb")
+
+
+class CostModel:
+    """Fitted decode-cost model; see the module docstring for its terms."""
+
+    def __init__(self, rows: list[dict], compute_units: int = 256):
+        from scipy.optimize import nnls
+
+        self.compute_units = compute_units
+        shapes = [StepShape(r["batch"], r["q_heads"], r["kv_heads"], r["head_dim"], r["seq_len"], r["prefix"],
+                            r["window"], r["budget_pages"]) for r in rows]
+        feats = [_features(s, compute_units) for s in shapes]
+        xd = np.array([[1.0, f["dense_mb"]] for f in feats])
+        self.dense_coef = nnls(xd, np.array([r["dense_us"] for r in rows]))[0]
+        idx = [i for i, f in enumerate(feats) if not f["all_taken"]]
+        xs = np.array([_sparse_row(feats[i]) for i in idx])
+        self.sparse_coef = nnls(xs, np.array([rows[i]["sparse_us"] for i in idx]))[0]
+
+    @property
+    def terms(self) -> dict:
+        return dict(zip(SPARSE_TERMS + DENSE_TERMS, [float(c) for c in self.sparse_coef] +
+                        [float(c) for c in self.dense_coef]))
+
+    def dense_us(self, s: StepShape) -> float:
+        f = _features(s, self.compute_units)
+        return float(self.dense_coef @ np.array([1.0, f["dense_mb"]]))
+
+    def sparse_us(self, s: StepShape) -> float:
+        f = _features(s, self.compute_units)
+        if f["all_taken"]:
+            return self.dense_us(s)
+        return float(self.sparse_coef @ np.array(_sparse_row(f)))
+
+    def layer_cost(self, s: StepShape) -> dict:
+        """Predicted sparse and dense step times and their ratio for one layer."""
+        sp, de = self.sparse_us(s), self.dense_us(s)
+        return {"sparse_us": sp, "dense_us": de, "speedup_vs_dense": de / sp}
+
+
+def load(path: str = _DATA) -> CostModel:
+    """The model fitted to the packaged MI355X measurements."""
+    data = json.load(open(path))
+    return CostModel(data["rows"], data.get("compute_units", 256))
