@@ -262,6 +262,71 @@ def calibrate(steps, warmup):
     return rows
 
 
+def layers12(steps, warmup):
+    """One decode step of a 12-layer model at 128k context: for each layer (its
+    own KV cache, metadata and per-layer prefix/window/budget of the 12-layer
+    sweep), append the new token's K/V and run the sparse decode.  Timed as
+    eager launches and as a captured HIP graph of two model steps (the
+    sequence lengths ping-pong between two buffers)."""
+    import torch
+
+    import free_sparse_attention_amd as fsa
+    import synth
+    from tests.gpu_harness import DeviceWorkload, to_dev_bf16
+
+    extra = 2 * (warmup + steps) + 16
+    layers = []
+    for l in range(12):
+        wl = synth.make_workload("sweep12", layer=l, extra_tokens=extra)
+        layers.append(DeviceWorkload(wl))
+        log(f"[layers12] layer {l}: cfg {wl.cfg}")
+    wl0 = layers[0].wl
+    msl = int(wl0.seq_lens.max()) + extra
+    lens = [layers[0].seq_lens.clone(), torch.empty_like(layers[0].seq_lens)]
+    kn = to_dev_bf16(np.zeros((wl0.batch, 1, wl0.hkv, wl0.d), np.uint16) + 0x3F80)
+    vn = kn.clone()
+    outs = [torch.empty((wl0.batch, wl0.hq, wl0.d), dtype=torch.bfloat16, device="cuda") for _ in layers]
+    wss = [dw.workspace(max_seq_len=msl) for dw in layers]
+
+    def model_step(i, stream):
+        a, b = lens[i % 2], lens[(i + 1) % 2]
+        for dw, out, ws in zip(layers, outs, wss):
+            fsa.append_kv(dw.dims, 1, kn, vn, dw.page_table, a, b, dw.k_cache, dw.v_cache, dw.meta, stream)
+            fsa.sparse_decode_attn(dw.dims, dw.cfg(), dw.wl.sm_scale, msl, dw.q, dw.k_cache, dw.v_cache, dw.meta,
+                                   dw.page_table, b, out, None, ws, stream)
+
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(warmup):
+        model_step(i, stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        model_step(warmup + i, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_us = 1000.0 * e0.elapsed_time(e1) / steps
+    done = warmup + steps  # even, so lens[0] holds the current lengths again
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        model_step(0, torch.cuda.current_stream())
+        model_step(1, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    reps = steps // 2
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    graph_us = 1000.0 * e0.elapsed_time(e1) / (2 * reps)
+    assert int(lens[0].max()) <= msl and done % 2 == 0
+    del layers, wss, outs, g
+    torch.cuda.empty_cache()
+    return {"layers": 12, "seq_len": int(wl0.seq_lens.max()), "eager_us_per_model_step": eager_us,
+            "graph_us_per_model_step": graph_us, "eager_us_per_layer": eager_us / 12,
+            "graph_us_per_layer": graph_us / 12}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +338,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="instead: sparse vs dense step time for context lengths 2k..256k")
+    ap.add_argument("--layers12", action="store_true",
+                    help="instead: 12-layer model step (append + decode per layer), eager and as a HIP graph")
     ap.add_argument("--calibrate", action="store_true",
                     help="instead: step times over a grid of lengths, group sizes and layer configurations")
     args = ap.parse_args()
@@ -284,6 +351,15 @@ def main():
     synth.lib()
     import free_sparse_attention_amd as fsa
     fsa.load()
+
+    if args.layers12:
+        r = layers12(max(20, args.steps // 4), 4)
+        print(json.dumps({"metric": "12-layer decode model step (append + sparse decode per layer)", "unit": "us",
+                          "n_gpus": 1, "data": "synthetic (seeded)",
+                          "config": {"workload": "sweep12 (128k context, per-layer prefix/window/budget)",
+                                     "batch": 4, "q_heads": 16, "kv_heads": 4, "head_dim": 128},
+                          "result": r}), flush=True)
+        return
 
     if args.calibrate:
         rows = calibrate(max(20, args.steps // 4), args.warmup)
