@@ -171,17 +171,23 @@ __device__ __forceinline__ void merge_waves(MergeLds<D, WAVES>& S, const WaveAtt
   // per head: the maximum, the waves' weights and the weighted sum, once
   if (threadIdx.x < 16) {
     const int h = threadIdx.x;
+    float mw[WAVES], lw[WAVES];  // all reads first, so they are in flight together
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      mw[w] = S.m[w][h];
+      lw[w] = S.l[w][h];
+    }
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, S.m[w][h]);
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mw[w]);
     float l = 0.f;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) {
-      const float mw = S.m[w][h];
-      const float e = mw == -INFINITY ? 0.f : exp2f(mw - M);
-      S.e[w][h] = e;
-      l += e * S.l[w][h];
+      mw[w] = mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - M);
+      l += mw[w] * lw[w];
     }
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) S.e[w][h] = mw[w];
     S.M[h] = M;
     S.L[h] = l;
   }

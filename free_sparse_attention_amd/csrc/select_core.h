@@ -49,7 +49,7 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 
 struct SelectLds {
   int32_t sphys[kSelMaxPages];  // page-table entries of pages [0, n_max)
-  uint32_t hist[2][kSelBins];
+  uint32_t hist[2][kSelBins + kWave];  // bins, then one discard slot per lane
   __attribute__((aligned(16))) uint32_t cnt[2][kSelCols * kSelWaves];  // per-word popcounts
   uint32_t mm[2 * kSelWaves];
   uint32_t s_prefix, s_need, s_done;
@@ -197,7 +197,10 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
 #pragma unroll
         for (int j = 0; j < COLS; ++j) {
           const uint32_t d = key[j] >> shift;  // shift + width <= 32, so d >> width is defined
-          if (((cand >> j) & 1u) && (d >> width) == kprefix) atomicAdd(&h[d & ((1u << width) - 1u)], 1u);
+          // every lane adds: pages outside the digit's range go to the lane's discard
+          // slot, so the loop has no per-page branch
+          const bool in = ((cand >> j) & 1u) && (d >> width) == kprefix;
+          atomicAdd(&h[in ? (d & ((1u << width) - 1u)) : kSelBins + lane], 1u);
         }
         for (int i = tid; i < kSelBins; i += kSelThreads) h_next[i] = 0;  // for the next pass
         __syncthreads();
