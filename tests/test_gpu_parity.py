@@ -164,6 +164,24 @@ def test_shapes(d, hq, hkv):
     run_and_check(wl)
 
 
+@pytest.mark.parametrize("budget", [40, 80])
+def test_many_units_both_step_plans(budget):
+    """64 (sequence, KV head) units: budget 40 fits selection replicas with two
+    selected pages per wave on half the CUs (wide plan), budget 80 does not
+    (narrow plan, split-K launch over the selected pages)."""
+    wl = synth.workloads.build(name=f"units{budget}", seed=18, batch=8, hq=16, hkv=8, d=64,
+                               seq_lens=(4000, 2500, 3333, 1900, 4096, 3000, 2222, 3900), prefix=48, window=300,
+                               budget=budget, k_sigma=0.5, n_needles=4, permuted=True)
+    run_and_check(wl, units=[(0, 0), (1, 7), (4, 3), (7, 5), (2, 2)])
+
+
+def test_longest_contexts_32_pages_per_thread():
+    """Over 16384 pages (256k tokens) the selection holds 32 pages per thread."""
+    wl = synth.workloads.build(name="long", seed=19, batch=1, hq=8, hkv=1, d=128, seq_lens=(400001,), prefix=128,
+                               window=4096, budget=256, k_sigma=0.5, n_needles=16, permuted=True)
+    run_and_check(wl, dense=False)
+
+
 @pytest.mark.parametrize("cfg", [(0, 0, 5), (0, 300, 0), (100, 0, 0), (37, 53, 6), (64, 256, 10**5),
                                  (5000, 16, 3), (16, 5000, 3), (0, 1, 1)])
 def test_configs_and_degenerate_regions(cfg):
