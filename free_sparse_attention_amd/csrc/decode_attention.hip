@@ -13,6 +13,7 @@
 // (the prefix and window attention beside the selection): slots_per_unit
 // counts them all, and this kernel's workgroups start at slot_base.
 #include <algorithm>
+#include <atomic>
 
 #include "attend_core.h"
 
@@ -158,9 +159,12 @@ __global__ __launch_bounds__(256) void combine_kernel(
 AttnPlan plan_attention(int units, int max_items) {
   // one resident round of waves (3 workgroups of 4 waves per CU) shared out
   // over all items; longer runs per wave when there is more work
-  static int res = 0;
-  if (res == 0)
+  static std::atomic<int> cached{0};
+  int res = cached.load(std::memory_order_relaxed);
+  if (res == 0) {
     res = resident_blocks_per_cu(reinterpret_cast<const void*>(&decode_attention_kernel<128, kList>), 256);
+    cached.store(res, std::memory_order_relaxed);
+  }
   const long round_waves = (long)res * device_cu_count() * kAttnWaves;
   const long total = (long)units * std::max(1, max_items);
   int ipw = (int)((total + round_waves - 1) / round_waves);

@@ -1,12 +1,16 @@
 // Device properties used to size grids: compute-unit count and how many
 // workgroups of a kernel fit on one compute unit.  Values are cached after
-// the first query (one device model per process is assumed).
+// the first query (one device model per process is assumed); concurrent
+// first calls may both query, with the same result.
+#include <atomic>
+
 #include "fsa_internal.h"
 
 namespace fsa {
 
 int device_cu_count() {
-  static int n = 0;
+  static std::atomic<int> cached{0};
+  int n = cached.load(std::memory_order_relaxed);
   if (n == 0) {
     int dev = 0, c = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
@@ -14,6 +18,7 @@ int device_cu_count() {
       n = c;
     else
       n = 256;  // MI355X
+    cached.store(n, std::memory_order_relaxed);
   }
   return n;
 }

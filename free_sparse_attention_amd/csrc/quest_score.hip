@@ -22,6 +22,7 @@
 // s reads values 8 gq .. 8 gq + 7 of page col, so every load instruction is
 // fully coalesced and no page table is involved.
 #include <algorithm>
+#include <atomic>
 
 #include "fsa_internal.h"
 
@@ -139,9 +140,12 @@ hipError_t launch_quest_scores(const uint16_t* q, const uint16_t* meta, const in
   const int tiles_per_unit = (max_cand + kMetaTile - 1) / kMetaTile + 1;  // a range may straddle one more
   const void* kern = d == 128 ? reinterpret_cast<const void*>(&quest_score_kernel<128>)
                               : reinterpret_cast<const void*>(&quest_score_kernel<64>);
-  static int resident[2] = {0, 0};
-  int& res = resident[d == 128];
-  if (res == 0) res = resident_blocks_per_cu(kern, 256);
+  static std::atomic<int> resident[2];  // per head dim, zero until first queried
+  int res = resident[d == 128].load(std::memory_order_relaxed);
+  if (res == 0) {
+    res = resident_blocks_per_cu(kern, 256);
+    resident[d == 128].store(res, std::memory_order_relaxed);
+  }
   // one resident round of workgroups shared out over the units
   const int round = res * device_cu_count();
   const int wg_per_unit_max = (tiles_per_unit + 3) / 4;
