@@ -264,16 +264,23 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
       tie_take |= (uint32_t)(tied && rank < need) << j;
     }
   }
-  // taken pages: bit j of `mine`
+  // taken pages: bit j of `mine` (one uniform branch, then a lean per-page test)
   uint32_t mine = 0, wc = 0;
+  if (!radix) {
+    mine = k == C ? cand : 0u;
+  } else if (done) {  // the threshold digit's bin is taken whole
+#pragma unroll
+    for (int j = 0; j < COLS; ++j) mine |= (uint32_t)((key[j] >> shift) >= kprefix) << j;
+    mine &= cand;
+  } else {  // keys above the threshold, and the tied pages ranked in
+#pragma unroll
+    for (int j = 0; j < COLS; ++j) mine |= (uint32_t)((key[j] >> shift) > kprefix) << j;
+    mine = (mine | tie_take) & cand;
+  }
 #pragma unroll
   for (int j = 0; j < COLS; ++j) {
-    const uint32_t kt = key[j] >> shift;
-    const bool above = radix ? (kt > kprefix || (kt == kprefix && (done || ((tie_take >> j) & 1u)))) : k == C;
-    const bool t = ((cand >> j) & 1u) && above;
-    const unsigned long long g = __ballot(t);
+    const unsigned long long g = __ballot((mine >> j) & 1u);
     wc = lane == j ? (uint32_t)__popcll(g) : wc;
-    mine |= (uint32_t)t << j;
   }
   if (lane < COLS) S.cnt[1][lane * kSelWaves + wave] = wc;
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's page-table entries have landed in LDS
