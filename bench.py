@@ -327,6 +327,75 @@ def layers12(steps, warmup):
             "graph_us_per_layer": graph_us / 12}
 
 
+def ragged_serving(steps, warmup):
+    """The 16-sequence serving batch (lengths 16k..256k, Hq 32 / Hkv 8, D 128,
+    prefix 128, window 2048, budget 256, one shared permuted pool): a step is
+    one-token append to every sequence followed by the sparse decode."""
+    import torch
+
+    import free_sparse_attention_amd as fsa
+    import synth
+    from tests.gpu_harness import DeviceWorkload, to_dev_bf16
+
+    wl = synth.make_workload("ragged16", extra_tokens=2 * (warmup + steps) + 16)
+    dw = DeviceWorkload(wl)
+    msl = int(wl.seq_lens.max()) + 2 * (warmup + steps) + 16
+    lens = [dw.seq_lens.clone(), torch.empty_like(dw.seq_lens)]
+    kn = to_dev_bf16(np.zeros((wl.batch, 1, wl.hkv, wl.d), np.uint16) + 0x3F80)
+    vn = kn.clone()
+    out = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.bfloat16, device="cuda")
+    ws = dw.workspace(max_seq_len=msl)
+    c = dw.cfg()
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        a, b = lens[i % 2], lens[(i + 1) % 2]
+        fsa.append_kv(dw.dims, 1, kn, vn, dw.page_table, a, b, dw.k_cache, dw.v_cache, dw.meta, stream)
+        fsa.sparse_decode_attn(dw.dims, c, wl.sm_scale, msl, dw.q, dw.k_cache, dw.v_cache, dw.meta, dw.page_table,
+                               b, out, None, ws, stream)
+
+    dws = dw.dense_workspace(max_seq_len=msl)
+
+    def dense_step(i):
+        a, b = lens[i % 2], lens[(i + 1) % 2]
+        fsa.append_kv(dw.dims, 1, kn, vn, dw.page_table, a, b, dw.k_cache, dw.v_cache, dw.meta, stream)
+        fsa.dense_decode_attn(dw.dims, wl.sm_scale, msl, dw.q, dw.k_cache, dw.v_cache, dw.page_table, b, out,
+                              dws, stream)
+
+    def run(fn, first, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(first + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return 1000.0 * e0.elapsed_time(e1) / n
+
+    # the two step kinds each append `warmup + steps` tokens per sequence
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    us = run(step, warmup, steps)
+    n0 = warmup + steps
+    for i in range(warmup):
+        dense_step(n0 + i)
+    torch.cuda.synchronize()
+    dense_us = run(dense_step, n0 + warmup, steps)
+    L = wl.seq_lens.astype(np.int64)
+    P, W, budget = wl.cfg
+    n = -(-L // wl.page)
+    Pe, Ws = np.minimum(P, L), np.maximum(0, L - W)
+    C = np.where(Pe < Ws, -(-Ws // wl.page) - Pe // wl.page, 0)
+    k = np.minimum(budget, C)
+    T = Pe + (L - np.maximum(Ws, Pe)) + np.minimum(k * wl.page, np.maximum(0, Ws - Pe))
+    alg = int((wl.hkv * (4 * wl.d * C + 4 * wl.d * T + 4 * wl.group * wl.d) + 4 * n).sum())
+    del dw
+    torch.cuda.empty_cache()
+    return {"sequences": wl.batch, "seq_len_min": int(L.min()), "seq_len_max": int(L.max()),
+            "us_per_step": us, "steps_per_s": 1e6 / us, "step_alg_bytes": alg, "step_GBps": alg / us / 1e3,
+            "dense_us_per_step": dense_us, "speedup_vs_dense": dense_us / us}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,6 +407,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="instead: sparse vs dense step time for context lengths 2k..256k")
+    ap.add_argument("--ragged", action="store_true",
+                    help="instead: the 16-sequence serving batch, one-token append + sparse decode per step")
     ap.add_argument("--layers12", action="store_true",
                     help="instead: 12-layer model step (append + decode per layer), eager and as a HIP graph")
     ap.add_argument("--calibrate", action="store_true",
@@ -351,6 +422,15 @@ def main():
     synth.lib()
     import free_sparse_attention_amd as fsa
     fsa.load()
+
+    if args.ragged:
+        r = ragged_serving(max(20, args.steps // 4), 4)
+        print(json.dumps({"metric": "serving step (append + sparse decode), 16 ragged sequences", "unit": "us",
+                          "n_gpus": 1, "data": "synthetic (seeded)",
+                          "config": {"workload": "ragged16", "batch": 16, "q_heads": 32, "kv_heads": 8,
+                                     "head_dim": 128, "prefix": 128, "window": 2048, "budget_pages": 256},
+                          "result": r}), flush=True)
+        return
 
     if args.layers12:
         r = layers12(max(20, args.steps // 4), 4)

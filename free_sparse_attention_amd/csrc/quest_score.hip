@@ -36,9 +36,13 @@ __device__ __forceinline__ uint32_t keep_sign(uint32_t w, bool negative) {
   return negative ? (w & neg_mask) : (w & ~neg_mask);
 }
 
-// Each wave scores a contiguous run of 16-page tiles of one (sequence, KV head)
-// unit; the grid is sized to one resident round of waves.  Metadata is loaded
-// one tile ahead of the MFMA chain.
+// Each wave scores every W-th 16-page tile of one (sequence, KV head) unit,
+// W being the unit's wave count, so at any moment the unit's waves together
+// read one contiguous stretch of metadata; the grid is sized to one resident
+// round of waves.  Metadata is loaded one tile ahead of the MFMA chain, with
+// the non-temporal hint: it is read once per step and should not displace
+// cached data (on MI355X this streams about a quarter faster at 256k tokens
+// than plain loads or a contiguous run of tiles per wave).
 template <int D>
 __global__ __launch_bounds__(256) void quest_score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ meta,
@@ -54,7 +58,8 @@ __global__ __launch_bounds__(256) void quest_score_kernel(
   // tile is known before the length arrives and is loaded together with it.
   const int c_lo_h = min(prefix, max_seq_len) / kPage;
   const int c_hi_h = (max(0, max_seq_len - window) + kPage - 1) / kPage;
-  const int t_first = c_lo_h / kMetaTile + (wg * 4 + wave) * tiles_per_wave;
+  const int n_waves = 4 * wg_per_unit;
+  const int t_first = c_lo_h / kMetaTile + wg * 4 + wave;  // then every n_waves-th tile
   const int t_end_h = max(1, (c_hi_h + kMetaTile - 1) / kMetaTile);
 
   // A operand: row `col` = query head col of the group (zero beyond G).
@@ -81,7 +86,7 @@ __global__ __launch_bounds__(256) void quest_score_kernel(
     // first tile, clamped into the host bound's range (used only if valid below)
     const uint16_t* src = mbase + (size_t)min(t_first, t_end_h - 1) * (NSTEP * kMetaTile * 32);
 #pragma unroll
-    for (int s = 0; s < NSTEP; ++s) bufA[s] = *reinterpret_cast<const uint4*>(src + s * (kMetaTile * 32));
+    for (int s = 0; s < NSTEP; ++s) bufA[s] = ld_nt(reinterpret_cast<const uint4*>(src + s * (kMetaTile * 32)));
   }
   const int L = min(seq_lens[b], max_seq_len);  // lengths beyond the host bound are clamped
   const int Pe = min(prefix, L), Ws = max(0, L - window);
@@ -89,14 +94,14 @@ __global__ __launch_bounds__(256) void quest_score_kernel(
   const int c_lo = Pe / kPage, c_hi = (Ws + kPage - 1) / kPage;  // c_lo == c_lo_h here
   const int t_end = (c_hi + kMetaTile - 1) / kMetaTile;
   if (t_first >= t_end) return;
-  const int n_tiles = min(tiles_per_wave, t_end - t_first);
+  const int n_tiles = min(tiles_per_wave, (t_end - t_first + n_waves - 1) / n_waves);
   // Loads are unconditional (tiles are whole; pages outside the candidates
   // are scored but not stored), so the number of loads in flight is the same
   // on every path and the compiler waits only for the tile about to be reduced.
   auto load = [&](int t, uint4 (&buf)[NSTEP]) {
-    const uint16_t* src = mbase + (size_t)(t_first + t) * (NSTEP * kMetaTile * 32);
+    const uint16_t* src = mbase + (size_t)(t_first + t * n_waves) * (NSTEP * kMetaTile * 32);
 #pragma unroll
-    for (int s = 0; s < NSTEP; ++s) buf[s] = *reinterpret_cast<const uint4*>(src + s * (kMetaTile * 32));
+    for (int s = 0; s < NSTEP; ++s) buf[s] = ld_nt(reinterpret_cast<const uint4*>(src + s * (kMetaTile * 32)));
   };
   auto compute = [&](int t, const uint4 (&buf)[NSTEP]) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -110,7 +115,7 @@ __global__ __launch_bounds__(256) void quest_score_kernel(
       if (4 * gq + r < G) sc = fmaxf(sc, acc[r]);
     if (G > 4) sc = fmaxf(sc, __shfl_xor(sc, 16));
     if (G > 8) sc = fmaxf(sc, __shfl_xor(sc, 32));
-    const int p = (t_first + t) * kMetaTile + col;
+    const int p = (t_first + t * n_waves) * kMetaTile + col;
     if (gq == 0 && p >= c_lo && p < c_hi) srow[p] = sc;
   };
 
