@@ -374,6 +374,8 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
   sa.slots_per_unit = w.slots;
   sa.pw_ipw = w.step.pw.ipw;
   sa.pw_wg = w.step.pw.wg_per_unit;
+  sa.sel_blocks = w.step.sel_blocks;
+  sa.xcd_grouped = w.step.xcd_grouped;
   sa.scale_log2 = sm_scale * 1.4426950408889634f;
   FSA_CHECK(hip_status(fsa::launch_select_attend(sa, st), "selection launch"));
   fsa::AttnArgs a = attn_args(dims, w.step.sel_items, sm_scale, max_seq_len, q, k_cache, v_cache, page_table, seq_lens,

@@ -8,6 +8,7 @@ namespace fsa {
 
 constexpr int kPage = 16;  // tokens per page
 constexpr int kWave = 64;  // CDNA wavefront width
+constexpr int kXcds = 8;   // MI355X: accelerator dies (XCDs), 32 CUs and one L2 each
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
@@ -171,6 +172,8 @@ struct StepArgs {
   int slots_per_unit;  // prefix/window workgroups first, then the selection replicas (wide)
   int pw_ipw;          // prefix/window items per wave
   int pw_wg;           // prefix/window workgroups per unit
+  int sel_blocks;      // selection workgroups at the front of the grid
+  int xcd_grouped;     // wide plan: workgroup -> (unit, replica) keeps a unit on one XCD
   float scale_log2;
 };
 
@@ -188,6 +191,8 @@ constexpr int kSliceMax = 256;  // selected items one replica can take
 struct StepPlan {
   int sel_rep, per, sel_items;
   PwPlan pw;
+  int sel_blocks;   // selection workgroups at the front of the grid
+  int xcd_grouped;  // wide plan: a unit's replicas share one XCD (see the kernel)
 };
 StepPlan plan_step(int units, int prefix, int window, int budget, int max_seq_len);
 hipError_t launch_select_attend(const StepArgs& a, hipStream_t stream);

@@ -159,9 +159,13 @@ __device__ __forceinline__ void select_and_attend(SelectLds& SL, MergeLds<D, kSe
   merge_waves<D, kSelWaves>(SM, st, G, false, nullptr, A.part_o + slot * G * D, A.part_ml + 2 * slot * G);
 }
 
-// Workgroups, in launch order: the selection workgroups (sel_rep per unit in
-// the wide plan, one per unit in the narrow plan), then pw_wg prefix/window
-// workgroups per unit.
+// Workgroups, in launch order: sel_blocks selection workgroups (sel_rep per
+// unit in the wide plan, one per unit in the narrow plan), then pw_wg
+// prefix/window workgroups per unit.  Workgroup i runs on XCD i % 8 (the
+// dispatcher deals workgroups round-robin over the XCDs); when xcd_grouped is
+// set, i = 8 (m sel_rep + r) + x is replica r of unit 8 m + x, so all replicas
+// of a unit share one XCD's L2: its scores and page-table row are fetched from
+// memory once, not once per replica (ids of absent units exit at once).
 template <int COLS, int D>
 __global__ __launch_bounds__(kSelThreads) void select_attend_kernel(const StepArgs A) {
   __shared__ union {
@@ -170,10 +174,17 @@ __global__ __launch_bounds__(kSelThreads) void select_attend_kernel(const StepAr
   } U;
   __shared__ int4 slice[kSliceMax];
   const int units = A.batch * A.hkv;
-  const int n_sel = units * (A.sel_rep > 0 ? A.sel_rep : 1);
-  if ((int)blockIdx.x < n_sel) {
+  const int i = blockIdx.x;
+  if (i < A.sel_blocks) {
     if (A.sel_rep > 0) {
-      select_and_attend<COLS, D>(U.sel, U.att, slice, A, blockIdx.x / A.sel_rep, blockIdx.x % A.sel_rep);
+      int unit = i / A.sel_rep, r = i % A.sel_rep;
+      if (A.xcd_grouped) {
+        const int k = i / kXcds;
+        unit = i % kXcds + kXcds * (k / A.sel_rep);
+        r = k % A.sel_rep;
+        if (unit >= units) return;
+      }
+      select_and_attend<COLS, D>(U.sel, U.att, slice, A, unit, r);
     } else {
       // narrow plan: the selected items go to the work list of the split-K
       // attention kernel
@@ -183,7 +194,7 @@ __global__ __launch_bounds__(kSelThreads) void select_attend_kernel(const StepAr
       select_unit<COLS>(U.sel, J);
     }
   } else {
-    const int w = blockIdx.x - n_sel;
+    const int w = i - A.sel_blocks;
     prefix_window_attend<D>(U.att, A, w / A.pw_wg, w % A.pw_wg);
   }
 }
@@ -253,11 +264,15 @@ StepPlan plan_step(int units, int prefix, int window, int budget, int max_seq_le
   }
   const int busy = units * std::max(1, p.sel_rep);
   p.pw = plan_prefix_window(units, busy, prefix, window, max_seq_len);
+  // a unit's replicas on one XCD when every XCD's share stays within half its CUs
+  const int per_xcd = (units + kXcds - 1) / kXcds * p.sel_rep;
+  p.xcd_grouped = p.sel_rep > 0 && per_xcd <= cus / kXcds / 2;
+  p.sel_blocks = p.xcd_grouped ? kXcds * per_xcd : busy;
   return p;
 }
 
 hipError_t launch_select_attend(const StepArgs& a, hipStream_t stream) {
-  const unsigned grid = (unsigned)(a.batch * a.hkv * ((a.sel_rep > 0 ? a.sel_rep : 1) + a.pw_wg));
+  const unsigned grid = (unsigned)(a.sel_blocks + a.batch * a.hkv * a.pw_wg);
 #define FSA_SA(C, DD) hipLaunchKernelGGL((select_attend_kernel<C, DD>), dim3(grid), dim3(kSelThreads), 0, stream, a)
 #define FSA_SA_D(C)         \
   do {                      \
