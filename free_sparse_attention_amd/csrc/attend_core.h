@@ -163,10 +163,11 @@ __device__ __forceinline__ void merge_waves(MergeLds<D, WAVES>& S, const WaveAtt
     S.m[wave][col] = st.m;
     S.l[wave][col] = st.l;
   }
+  if (col < G)  // columns beyond the group's heads are padding (LDS bandwidth bounds this phase)
 #pragma unroll
-  for (int t = 0; t < NDT; ++t)
+    for (int t = 0; t < NDT; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) S.o[wave][16 * t + 4 * gq + r][col] = st.acc[t][r];
+      for (int r = 0; r < 4; ++r) S.o[wave][16 * t + 4 * gq + r][col] = st.acc[t][r];
   __syncthreads();
   // per head: the maximum, the waves' weights and the weighted sum, once
   if (threadIdx.x < 16) {
