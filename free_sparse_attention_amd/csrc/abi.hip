@@ -125,7 +125,7 @@ SparseWs sparse_ws(const fsa_dims* d, fsa_layer_cfg c, int32_t max_seq_len) {
     w.plan = fsa::plan_attention(units, n_pages_max(max_seq_len));
     w.slots = w.plan.wg_per_unit;
   } else {
-    w.step = fsa::plan_step(units, c.prefix_tokens, c.window_tokens, c.budget_pages, max_seq_len);
+    w.step = fsa::plan_step(units, d->head_dim, c.prefix_tokens, c.window_tokens, c.budget_pages, max_seq_len);
     if (w.step.sel_rep > 0) {
       w.plan = fsa::AttnPlan{0, 0};
       w.slots = w.step.pw.wg_per_unit + w.step.sel_rep;
@@ -376,6 +376,7 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
   sa.pw_wg = w.step.pw.wg_per_unit;
   sa.sel_blocks = w.step.sel_blocks;
   sa.xcd_grouped = w.step.xcd_grouped;
+  sa.prefetch = w.step.prefetch;
   sa.scale_log2 = sm_scale * 1.4426950408889634f;
   FSA_CHECK(hip_status(fsa::launch_select_attend(sa, st), "selection launch"));
   fsa::AttnArgs a = attn_args(dims, w.step.sel_items, sm_scale, max_seq_len, q, k_cache, v_cache, page_table, seq_lens,

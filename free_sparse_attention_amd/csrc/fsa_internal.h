@@ -174,6 +174,7 @@ struct StepArgs {
   int pw_wg;           // prefix/window workgroups per unit
   int sel_blocks;      // selection workgroups at the front of the grid
   int xcd_grouped;     // wide plan: workgroup -> (unit, replica) keeps a unit on one XCD
+  int prefetch;        // wide plan: replicas prefetch known-taken pages into their L2
   float scale_log2;
 };
 
@@ -193,8 +194,9 @@ struct StepPlan {
   PwPlan pw;
   int sel_blocks;   // selection workgroups at the front of the grid
   int xcd_grouped;  // wide plan: a unit's replicas share one XCD (see the kernel)
+  int prefetch;     // wide plan: replicas prefetch known-taken pages into their L2
 };
-StepPlan plan_step(int units, int prefix, int window, int budget, int max_seq_len);
+StepPlan plan_step(int units, int head_dim, int prefix, int window, int budget, int max_seq_len);
 hipError_t launch_select_attend(const StepArgs& a, hipStream_t stream);
 
 // Attention work-item sources: every page of the sequence, or the selection's work list.

@@ -77,7 +77,15 @@ struct SelectJob {
   int sel_items;      // padded with empty items up to sel_items
   int4* slice;        // or null: selected items [slice_lo, slice_lo + slice_cap) go to
   int slice_lo, slice_cap;  // slice[o - slice_lo] (typically LDS)
+  // or null: after the first radix pass, pull into L2 the K and V blocks of
+  // some pages already known to be taken (this workgroup's share of them)
+  const uint16_t* pf_kc;
+  const uint16_t* pf_vc;
+  size_t pf_head_off, pf_page_stride;
+  int pf_rep, pf_r;
 };
+
+constexpr int kPrefetch = 4;  // prefetched pages per wave at most
 
 __device__ __forceinline__ void put_item(int32_t* work, int idx, int p, int phys, int lo, int hi) {
   *reinterpret_cast<int4*>(work + 4 * (size_t)idx) = make_int4(p, phys, lo, hi);
@@ -106,12 +114,48 @@ __device__ __forceinline__ uint32_t wave_word_prefix(const uint32_t* cnt, int nw
   return pre;
 }
 
+// Pages already known to be taken (candidates whose shifted key lies above
+// the threshold digit, or in it when that digit is taken whole) have their K
+// and V blocks requested into L2.  The pages are split over the pf_rep
+// workgroups by lane (lane mod pf_rep == pf_r); each such lane offers its first
+// known-taken page, and the wave fetches the first kPrefetch pages offered,
+// one load instruction per page: lanes 0-31 touch the 32 128-byte lines of the
+// K block, lanes 32-63 those of the V block.  The loaded words are returned so
+// that the caller keeps them live (and so waits for them) only where it waits
+// for later loads anyway.
+template <int COLS>
+__device__ __forceinline__ void prefetch_taken(const SelectLds& S, const SelectJob& J, const uint32_t (&key)[COLS],
+                                               uint32_t cand, int shift, uint32_t kprefix, bool done, int tid,
+                                               int lane, uint32_t (&pf)[kPrefetch]) {
+  uint32_t taken = 0;  // bit j: page tid + 1024 j is known to be taken
+#pragma unroll
+  for (int j = 0; j < COLS; ++j) {
+    const uint32_t d = key[j] >> shift;
+    taken |= (uint32_t)(d > kprefix || (done && d == kprefix)) << j;
+  }
+  taken &= cand;
+  if (lane % J.pf_rep != J.pf_r) taken = 0;
+  const int j0 = taken ? __builtin_ctz(taken) : 0;
+  const int phys = S.sphys[tid + kSelThreads * j0];
+  unsigned long long m = __ballot(taken != 0);
+  const uint16_t* base = (lane < 32 ? J.pf_kc : J.pf_vc) + J.pf_head_off + (size_t)(lane & 31) * 64;
+#pragma unroll
+  for (int i = 0; i < kPrefetch; ++i) {
+    if (m) {
+      const int pp = __builtin_amdgcn_readlane(phys, __builtin_ctzll(m));
+      m &= m - 1;
+      pf[i] = *reinterpret_cast<const uint32_t*>(base + (size_t)pp * J.pf_page_stride);
+    }
+  }
+}
+
 // COLS: pages per thread, a power of two with 1024 COLS >= ceil(max_seq_len / 16)
 // (a compile-time trip count: the per-page loops carry no guards).
 // What the selection leaves its caller: k, the number of selected pages, and
 // L, the sequence length (clamped to the host bound).
 struct SelectResult {
   int k, L;
+  uint32_t pf[kPrefetch];  // words loaded by the prefetch (keep live until later loads are waited for)
 };
 
 // After the call, S.sphys[p] holds page_table[b][p] for p < n_max.
@@ -164,6 +208,8 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
   // ---- 2. exact k-th largest key: keys >> shift compared with kprefix, `need` ties to take
   uint32_t kprefix = 0, need = 0;
   int shift = 0;
+  uint32_t pf[kPrefetch] = {0u, 0u, 0u, 0u};
+  bool pt_landed = false;  // this wave has waited for its page-table entries
   bool done = false;  // the threshold's bin holds exactly the keys still needed
   if (radix) {
     need = (uint32_t)k;
@@ -236,6 +282,11 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
         kprefix = S.s_prefix;
         need = S.s_need;
         done = S.s_done;
+        if (pass == 0 && J.pf_kc) {
+          __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's page-table entries are in LDS
+          pt_landed = true;
+          prefetch_taken<COLS>(S, J, key, cand, shift, kprefix, done, tid, lane, pf);
+        }
         if (done || shift == 0) break;
         top = shift - 1;
       }
@@ -283,7 +334,9 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
     wc = lane == j ? (uint32_t)__popcll(g) : wc;
   }
   if (lane < COLS) S.cnt[1][lane * kSelWaves + wave] = wc;
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's page-table entries have landed in LDS
+  // this wave's page-table entries have landed in LDS (after a prefetch this
+  // was waited for already; waiting again would wait for the prefetch)
+  if (!pt_landed) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   const uint32_t P = wave_word_prefix(S.cnt[1], nwords, wave, lane);
   int32_t* selw = J.sel_work ? J.sel_work : (J.work ? J.work + 4 * n_pre : nullptr);  // item o of the selection
@@ -323,7 +376,7 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
                min(p * kPage + kPage, L) - p * kPage);
     }
   }
-  return SelectResult{k, L};
+  return SelectResult{k, L, {pf[0], pf[1], pf[2], pf[3]}};
 }
 
 }  // namespace fsa

@@ -34,6 +34,7 @@ __global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
   J.pt = page_table + (size_t)b * max_pages;
   J.seq_len = seq_lens + b;
   J.minmax = nullptr;
+  J.pf_kc = nullptr;
   J.max_seq_len = max_seq_len;
   J.prefix = prefix;
   J.window = window;
@@ -106,6 +107,7 @@ __device__ __forceinline__ SelectJob step_job(const StepArgs& A, int unit) {
   J.pt = A.page_table + (size_t)b * A.max_pages;
   J.seq_len = A.seq_lens + b;
   J.minmax = nullptr;
+  J.pf_kc = nullptr;
   J.max_seq_len = A.max_seq_len;
   J.prefix = A.prefix;
   J.window = A.window;
@@ -132,11 +134,24 @@ __device__ __forceinline__ void select_and_attend(SelectLds& SL, MergeLds<D, kSe
                                                   const StepArgs& A, int unit, int r) {
   const int b = unit / A.hkv, g = unit % A.hkv, G = A.hq / A.hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the query operand is loaded first, so that waiting for it later does not
+  // wait for the selection's prefetch loads (loads complete in order)
+  bf16x8_t qb[D / 32];
+  constexpr bool kCanPrefetch = COLS <= 8;  // beyond, the early query operand costs registers
+  if (kCanPrefetch) load_q_operand<D>(A.q + ((size_t)b * A.hq + (size_t)g * G) * D, G, qb);
   SelectJob J = step_job(A, unit);
   if (r != 0) J.sel = nullptr;
   J.slice = slice;
   J.slice_lo = r * A.per;
   J.slice_cap = A.per;
+  if (kCanPrefetch && A.prefetch) {  // the unit's replicas share an L2: each warms its share of the taken pages
+    J.pf_kc = A.kc;
+    J.pf_vc = A.vc;
+    J.pf_head_off = (size_t)g * (kPage * D);
+    J.pf_page_stride = (size_t)A.hkv * (kPage * D);
+    J.pf_rep = A.sel_rep;
+    J.pf_r = r;
+  }
   const SelectResult R = select_unit<COLS>(SL, J);
   __syncthreads();  // the slice is complete
   const int ipw = (A.per + kSelWaves - 1) / kSelWaves;
@@ -150,11 +165,12 @@ __device__ __forceinline__ void select_and_attend(SelectLds& SL, MergeLds<D, kSe
   }
   __syncthreads();  // every read of the selection's LDS precedes the merge that reuses it
   const int n = __popcll(__ballot(my_lo < my_hi));  // a prefix of the wave's lanes
-  bf16x8_t qb[D / 32];
-  load_q_operand<D>(A.q + ((size_t)b * A.hq + (size_t)g * G) * D, G, qb);
+  if (!kCanPrefetch) load_q_operand<D>(A.q + ((size_t)b * A.hq + (size_t)g * G) * D, G, qb);
   WaveAttn<D> st;
   attend_items<D, false>(A.kc, A.vc, (size_t)g * (kPage * D), (size_t)A.hkv * (kPage * D), qb, my_phys, my_lo,
                          my_hi, n, A.scale_log2, st);
+  // the prefetch words are used here, after the attention's own loads
+  asm volatile("" ::"v"(R.pf[0]), "v"(R.pf[1]), "v"(R.pf[2]), "v"(R.pf[3]));
   const size_t slot = (size_t)unit * A.slots_per_unit + A.pw_wg + r;
   merge_waves<D, kSelWaves>(SM, st, G, false, nullptr, A.part_o + slot * G * D, A.part_ml + 2 * slot * G);
 }
@@ -243,7 +259,7 @@ PwPlan plan_prefix_window(int units, int busy_cus, int prefix, int window, int m
   return p;
 }
 
-StepPlan plan_step(int units, int prefix, int window, int budget, int max_seq_len) {
+StepPlan plan_step(int units, int head_dim, int prefix, int window, int budget, int max_seq_len) {
   const int n_max = (max_seq_len + kPage - 1) / kPage;
   const int cus = device_cu_count();
   StepPlan p;
@@ -268,6 +284,11 @@ StepPlan plan_step(int units, int prefix, int window, int budget, int max_seq_le
   const int per_xcd = (units + kXcds - 1) / kXcds * p.sel_rep;
   p.xcd_grouped = p.sel_rep > 0 && per_xcd <= cus / kXcds / 2;
   p.sel_blocks = p.xcd_grouped ? kXcds * per_xcd : busy;
+  // prefetch of known-taken pages into the shared L2 while it holds them
+  // comfortably: the K and V blocks of one XCD's units' selections within
+  // half of its 4 MiB
+  const long xcd_bytes = (long)((units + kXcds - 1) / kXcds) * p.sel_items * 2 * kPage * head_dim * 2;
+  p.prefetch = p.xcd_grouped && xcd_bytes <= (2l << 20);
   return p;
 }
 
