@@ -106,6 +106,65 @@ def cpu_baseline(wl, budget_s=12.0):
                       f"{t_total:.1f} s; page metadata precomputed"}
 
 
+_PAR_UNITS = None  # prepared oracle units, inherited by the forked workers below
+
+
+def _oracle_unit(wl, prep):
+    import oracle
+
+    b, q, K, V, m, M = prep
+    P, W, budget = wl.cfg
+    L = int(wl.seq_lens[b])
+    cand = oracle.candidate_pages(L, P, W, wl.page)
+    s = oracle.group_score(oracle.quest_bound(q, m[cand], M[cand]))
+    sel = oracle.select_topk(s, cand, budget)
+    mask = oracle.attended_mask(L, P, W, wl.page, sel)
+    oracle.attend(q, K, V, mask, wl.sm_scale)
+
+
+def _par_worker(arg):
+    from threadpoolctl import threadpool_limits
+
+    idx, n_workers, budget_s = arg
+    wl, prepared = _PAR_UNITS
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while time.perf_counter() - t0 < budget_s:
+            _oracle_unit(wl, prepared[(idx + done * n_workers) % len(prepared)])
+            done += 1
+    return done
+
+
+def cpu_baseline_parallel(wl, workers=16, budget_s=10.0):
+    """The same oracle over independent (sequence, KV head) units in `workers`
+    forked processes (one thread each).  Runs before the process touches the
+    GPU: the workers are plain forks doing numpy work only."""
+    import multiprocessing as mp
+
+    import oracle
+
+    global _PAR_UNITS
+    prepared = []
+    for b in range(wl.batch):
+        for g in range(wl.hkv):
+            q, K, V = oracle.unit_inputs(wl, b, g)
+            m, M = oracle.page_minmax(K, wl.page)
+            prepared.append((b, q, K, V, m, M))
+    _PAR_UNITS = (wl, prepared)
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        done = sum(pool.map(_par_worker, [(i, workers, budget_s) for i in range(workers)]))
+    wall = time.perf_counter() - t0
+    _PAR_UNITS = None
+    steps = done / len(prepared)
+    return {"value": steps / wall, "unit": "steps/s", "cores": workers, "kind": "oracle",
+            "sample": f"{done} (sequence, KV head) units of the {wl.name} step ({steps:.2f} steps) by the float64 "
+                      f"numpy oracle in {workers} processes of one thread each, {wall:.1f} s wall; "
+                      f"page metadata precomputed"}
+
+
 def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
     import torch
 
@@ -145,6 +204,21 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
 
     log(f"[bench] {wl.name}: {warmup} warmup + {steps} timed steps")
     ms_step = timed(step, steps, warmup)
+    # spread: 20 repetitions of 50 steps
+    reps_us = sorted(1000.0 * timed(step, 50, 0) for _ in range(20))
+    # cold: single steps, each after a 1 GiB scrub that evicts L2 and the Infinity Cache
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold_us = []
+    for i in range(20):
+        scrub.add_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold_us.append(1000.0 * e0.elapsed_time(e1))
+    del scrub
+    cold_us.sort()
 
     # dominant kernel alone: the Quest scoring launch, same stream, same rotation
     scores = torch.empty((wl.batch, wl.hkv, wl.max_pages), dtype=torch.float32, device=dev)
@@ -159,7 +233,10 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
     res = {"ms_per_step": ms_step, "steps_per_s": 1000.0 / ms_step, "step_alg_bytes": step_bytes,
            "step_GBps": step_bytes / (ms_step * 1e-3) / 1e9, "score_ms": ms_score,
            "score_alg_bytes": score_bytes, "score_GBps": score_bytes / (ms_score * 1e-3) / 1e9,
-           "replicas": R}
+           "replicas": R,
+           "repetitions": {"reps": 20, "steps_each": 50, "median_us": reps_us[10], "p10_us": reps_us[2],
+                           "p90_us": reps_us[18]},
+           "cold_single_step_us": {"median": cold_us[10], "p10": cold_us[2], "p90": cold_us[18]}}
     if with_dense:
         dws = base.dense_workspace()
 
@@ -420,6 +497,10 @@ def main():
 
     import synth
     synth.lib()
+    par = None
+    if not (args.ragged or args.layers12 or args.calibrate or args.sweep or args.no_cpu_baseline):
+        # oracle in parallel processes first, while this process has not touched the GPU
+        par = cpu_baseline_parallel(synth.make_workload(args.workload))
     import free_sparse_attention_amd as fsa
     fsa.load()
 
@@ -489,10 +570,14 @@ def main():
                      "avg_launch_us": 1000.0 * r["score_ms"],
                      "alg_bytes_per_launch": r["score_alg_bytes"]},
         "cpu_baseline": cpu,
+        "cpu_baseline_parallel": par,
+        "repetitions": r["repetitions"],
+        "cold_single_step_us": r["cold_single_step_us"],
         "also": {k: {"steps_per_s": v["steps_per_s"], "ms_per_step": v["ms_per_step"],
                      "achieved_GBps": v["step_GBps"], "pct_hbm_peak": 100.0 * v["step_GBps"] / HBM_PEAK_GBS,
                      "speedup_vs_dense": v.get("speedup_vs_dense"), "score_GBps": v["score_GBps"],
-                     "score_us": 1000.0 * v["score_ms"]} for k, v in also.items()},
+                     "score_us": 1000.0 * v["score_ms"], "repetitions": v["repetitions"],
+                     "cold_single_step_us": v["cold_single_step_us"]} for k, v in also.items()},
         "detail": {k: v for k, v in r.items()},
     }
     print(json.dumps(line), flush=True)
