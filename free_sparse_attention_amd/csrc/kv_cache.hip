@@ -104,31 +104,46 @@ __global__ __launch_bounds__(64) void append_kv_kernel(
   if (t_lo >= t_hi) return;
   const int s0 = t_lo - p * kPage, s1 = t_hi - p * kPage;
   const size_t blk = (size_t)page_table[(size_t)b * max_pages + p] * hkv + g;
-  uint16_t* kdst = kc + blk * (kPage * D);
-  uint16_t* vdst = vc + blk * (kPage * D);
   const int tiles = meta_tiles(max_pages);
   const bool valid = slot >= s0 && slot < s1;
+  const bool merge = slot == 0 && s0 > 0;  // the page already holds tokens: merge with its metadata
+  // Every load first (new tokens, old metadata; one round trip beside the
+  // page-table entry), every store after: on this target a load wait also
+  // waits for earlier stores.
+  constexpr int NIT = NCH / 4;
+  uint4 kv[NIT], vv[NIT], om[NIT], oM[NIT];
 #pragma unroll
-  for (int it = 0; it < NCH / 4; ++it) {
+  for (int it = 0; it < NIT; ++it) {
     const int c = 4 * it + lane / kPage;
-    uint4 kv = make_uint4(0, 0, 0, 0);
+    kv[it] = vv[it] = om[it] = oM[it] = make_uint4(0, 0, 0, 0);
     if (valid) {
       const size_t src = (((size_t)b * n_new + (p * kPage + slot - L0)) * hkv + g) * D + c * 8;
-      kv = *reinterpret_cast<const uint4*>(k_new + src);
-      const uint4 vv = *reinterpret_cast<const uint4*>(v_new + src);
-      *reinterpret_cast<uint4*>(kdst + (c * kPage + slot) * 8) = kv;
-      const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+      kv[it] = *reinterpret_cast<const uint4*>(k_new + src);
+      vv[it] = *reinterpret_cast<const uint4*>(v_new + src);
+    }
+    if (merge) {
+      om[it] = *meta_min_chunk(meta, unit, p, c, tiles, D);
+      oM[it] = *meta_max_chunk(meta, unit, p, c, tiles, D);
+    }
+  }
+  uint16_t* kdst = kc + blk * (kPage * D);
+  uint16_t* vdst = vc + blk * (kPage * D);
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int c = 4 * it + lane / kPage;
+    if (valid) {
+      *reinterpret_cast<uint4*>(kdst + (c * kPage + slot) * 8) = kv[it];
+      const uint32_t w[4] = {vv[it].x, vv[it].y, vv[it].z, vv[it].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         vdst[(c * 8 + e) * kPage + slot] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
     }
     uint32_t mn[8], mx[8];
-    chunk_minmax(kv, valid, mn, mx);
+    chunk_minmax(kv[it], valid, mn, mx);
     if (slot == 0) {
-      if (s0 > 0) {  // the page already holds tokens: merge with its metadata
-        const uint4 om = *meta_min_chunk(meta, unit, p, c, tiles, D);
-        const uint4 oM = *meta_max_chunk(meta, unit, p, c, tiles, D);
-        const uint32_t a[4] = {om.x, om.y, om.z, om.w}, z[4] = {oM.x, oM.y, oM.z, oM.w};
+      if (merge) {
+        const uint32_t a[4] = {om[it].x, om[it].y, om[it].z, om[it].w};
+        const uint32_t z[4] = {oM[it].x, oM[it].y, oM[it].z, oM[it].w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           mn[e] = min(mn[e], bf16_order_key((a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
