@@ -183,7 +183,7 @@ struct StepArgs {
 struct PwPlan {
   int max_items, ipw, wg_per_unit;
 };
-PwPlan plan_prefix_window(int units, int busy_cus, int prefix, int window, int max_seq_len);
+PwPlan plan_prefix_window(int units, int pw_cus, int prefix, int window, int max_seq_len);
 
 // Plan of the step's selection launch: wide (sel_rep > 0) when selection
 // replicas with at most 2 selected pages per wave fit on half the CUs;

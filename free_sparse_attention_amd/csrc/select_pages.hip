@@ -240,7 +240,7 @@ hipError_t launch_select_pages(const float* scores, const int32_t* page_table,
   return hipGetLastError();
 }
 
-PwPlan plan_prefix_window(int units, int busy_cus, int prefix, int window, int max_seq_len) {
+PwPlan plan_prefix_window(int units, int pw_cus, int prefix, int window, int max_seq_len) {
   const int n_max = (max_seq_len + kPage - 1) / kPage;
   const int pre = std::min((prefix + kPage - 1) / kPage, n_max);
   const int win = std::min((window + kPage - 1) / kPage + 1, n_max);
@@ -251,8 +251,8 @@ PwPlan plan_prefix_window(int units, int busy_cus, int prefix, int window, int m
     p.wg_per_unit = 0;
     return p;
   }
-  // one workgroup per CU (the launch's LDS), on the CUs beside the selection's
-  const long waves = (long)std::max(1, device_cu_count() - busy_cus) * kSelWaves;
+  // one workgroup per CU at a time (the launch's LDS); pw_cus CUs' worth of workgroups
+  const long waves = (long)std::max(1, pw_cus) * kSelWaves;
   const long need = (long)units * p.max_items;
   p.ipw = (int)std::max<long>(1, std::min<long>(kWave, (need + waves - 1) / waves));
   p.wg_per_unit = (p.max_items + kSelWaves * p.ipw - 1) / (kSelWaves * p.ipw);
@@ -279,7 +279,11 @@ StepPlan plan_step(int units, int head_dim, int prefix, int window, int budget, 
     }
   }
   const int busy = units * std::max(1, p.sel_rep);
-  p.pw = plan_prefix_window(units, busy, prefix, window, max_seq_len);
+  // Wide plan: the prefix/window workgroups fill the CUs beside the replicas.
+  // Narrow plan: two rounds of them over every CU; the first take the
+  // CUs beside the selection, the rest the selection's CUs as they free up,
+  // so that each wave walks fewer pages (one page in flight per wave).
+  p.pw = plan_prefix_window(units, p.sel_rep > 0 ? cus - busy : 2 * cus, prefix, window, max_seq_len);
   // a unit's replicas on one XCD when every XCD's share stays within half its CUs
   const int per_xcd = (units + kXcds - 1) / kXcds * p.sel_rep;
   p.xcd_grouped = p.sel_rep > 0 && per_xcd <= cus / kXcds / 2;
