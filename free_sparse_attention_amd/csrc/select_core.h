@@ -63,26 +63,27 @@ __host__ __device__ inline int select_cols(int max_seq_len) {
   return c;
 }
 
-struct SelectJob {
-  const float* scores;     // the unit's scores, logical page p at [p]
-  const int32_t* pt;       // the sequence's page-table row
-  const int32_t* seq_len;  // the sequence's length (device)
-  const uint32_t* minmax;  // (max key, ~min key) of the candidates, or null: computed here
-  int max_seq_len;
-  int prefix, window, budget, max_items;
-  int32_t* work;    // the unit's work list, or null
-  int32_t* sel;     // the unit's selected pages, or null
-  int32_t* counts;  // the unit's (k, items), or null
-  int32_t* sel_work;  // or null: the selected items alone, (page, pool page, lo, hi) at [o],
-  int sel_items;      // padded with empty items up to sel_items
-  int4* slice;        // or null: selected items [slice_lo, slice_lo + slice_cap) go to
-  int slice_lo, slice_cap;  // slice[o - slice_lo] (typically LDS)
+struct SelectJob {  // every optional field defaults to null / zero
+  const float* scores = nullptr;     // the unit's scores, logical page p at [p]
+  const int32_t* pt = nullptr;       // the sequence's page-table row
+  const int32_t* seq_len = nullptr;  // the sequence's length (device)
+  const uint32_t* minmax = nullptr;  // (max key, ~min key) of the candidates, or null: computed here
+  int max_seq_len = 0;
+  int prefix = 0, window = 0, budget = 0, max_items = 0;
+  int32_t* work = nullptr;    // the unit's work list, or null
+  int32_t* sel = nullptr;     // the unit's selected pages, or null
+  int32_t* counts = nullptr;  // the unit's (k, items), or null
+  int32_t* sel_work = nullptr;  // or null: the selected items alone, (page, pool page, lo, hi) at [o],
+  int sel_items = 0;            // padded with empty items up to sel_items
+  int4* slice = nullptr;        // or null: selected items [slice_lo, slice_lo + slice_cap) go to
+  int slice_lo = 0, slice_cap = 0;  // slice[o - slice_lo] (typically LDS); with a slice, sel gets only
+                                    // those slots (and its padding only when slice_lo == 0)
   // or null: after the first radix pass, pull into L2 the K and V blocks of
   // some pages already known to be taken (this workgroup's share of them)
-  const uint16_t* pf_kc;
-  const uint16_t* pf_vc;
-  size_t pf_head_off, pf_page_stride;
-  int pf_rep, pf_r;
+  const uint16_t* pf_kc = nullptr;
+  const uint16_t* pf_vc = nullptr;
+  size_t pf_head_off = 0, pf_page_stride = 0;
+  int pf_rep = 1, pf_r = 0;
 };
 
 constexpr int kPrefetch = 4;  // prefetched pages per wave at most
@@ -340,7 +341,11 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
   __syncthreads();
   const uint32_t P = wave_word_prefix(S.cnt[1], nwords, wave, lane);
   int32_t* selw = J.sel_work ? J.sel_work : (J.work ? J.work + 4 * n_pre : nullptr);  // item o of the selection
-  const int slice_lo = J.slice_lo;
+  // Slots this call emits: with a slice only the slice's (its share of the
+  // selected pages and of sel), else all.  A column whose slots in this wave
+  // miss that range is skipped with one uniform test.
+  const int e_lo = J.slice ? J.slice_lo : 0;
+  const int e_hi = J.slice ? J.slice_lo + J.slice_cap : 0x7FFFFFFF;
 #pragma unroll
   for (int j = 0; j < COLS; ++j) {
     const bool t = (mine >> j) & 1u;
@@ -348,18 +353,19 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
     // read the word prefix with every lane active: a lane read inside the
     // branch below may be inactive and hold no defined value
     const int base = __builtin_amdgcn_readlane((int)P, 2 * j + (wave >> 3));
-    if (t) {
+    if (base < e_hi && base + (int)__popcll(g) > e_lo && t) {
       const int p = tid + kSelThreads * j;
       const int o = base + (int)lanes_below(g);
-      if (J.sel) J.sel[o] = p;
-      const int lo = max(p * kPage, Pe) - p * kPage, hi = min(p * kPage + kPage, Ws) - p * kPage;
-      if (selw) put_item(selw, o, p, S.sphys[p], lo, hi);
-      if (J.slice && (unsigned)(o - slice_lo) < (unsigned)J.slice_cap)
-        J.slice[o - slice_lo] = make_int4(p, S.sphys[p], lo, hi);
+      if (o >= e_lo && o < e_hi) {
+        if (J.sel) J.sel[o] = p;
+        const int lo = max(p * kPage, Pe) - p * kPage, hi = min(p * kPage + kPage, Ws) - p * kPage;
+        if (selw) put_item(selw, o, p, S.sphys[p], lo, hi);
+        if (J.slice) J.slice[o - e_lo] = make_int4(p, S.sphys[p], lo, hi);
+      }
     }
   }
   // Stores come last: on this target every load wait also waits for earlier stores.
-  if (J.sel)
+  if (J.sel && e_lo == 0)  // the padding, by the call whose slots start at 0
     for (int i = k + tid; i < J.budget; i += kSelThreads) J.sel[i] = -1;
   if (tid == 0 && J.counts) {
     J.counts[0] = k;

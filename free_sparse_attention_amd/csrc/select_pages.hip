@@ -140,7 +140,6 @@ __device__ __forceinline__ void select_and_attend(SelectLds& SL, MergeLds<D, kSe
   constexpr bool kCanPrefetch = COLS <= 8;  // beyond, the early query operand costs registers
   if (kCanPrefetch) load_q_operand<D>(A.q + ((size_t)b * A.hq + (size_t)g * G) * D, G, qb);
   SelectJob J = step_job(A, unit);
-  if (r != 0) J.sel = nullptr;
   J.slice = slice;
   J.slice_lo = r * A.per;
   J.slice_cap = A.per;
