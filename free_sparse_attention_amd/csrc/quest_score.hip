@@ -38,8 +38,8 @@ __device__ __forceinline__ uint32_t keep_sign(uint32_t w, bool negative) {
 
 // Each wave scores every W-th 16-page tile of one (sequence, KV head) unit,
 // W being the unit's wave count, so at any moment the unit's waves together
-// read one contiguous stretch of metadata; the grid is sized to one resident
-// round of waves.  Metadata is loaded one tile ahead of the MFMA chain, with
+// read one contiguous stretch of metadata; the grid is sized to four resident
+// rounds of waves.  Metadata is loaded one tile ahead of the MFMA chain, with
 // the non-temporal hint: it is read once per step and should not displace
 // cached data (on MI355X this streams about a quarter faster at 256k tokens
 // than plain loads or a contiguous run of tiles per wave).
@@ -151,8 +151,11 @@ hipError_t launch_quest_scores(const uint16_t* q, const uint16_t* meta, const in
     res = resident_blocks_per_cu(kern, 256);
     resident[d == 128].store(res, std::memory_order_relaxed);
   }
-  // one resident round of workgroups shared out over the units
-  const int round = res * device_cu_count();
+  // four resident rounds of workgroups shared out over the units: workgroups
+  // whose tiles lie beyond their sequence's length exit at once and the
+  // dispatcher gives their slots to the next ones, which evens out batches of
+  // unequal lengths (16 sequences of 18k-261k tokens: step 165.9 -> 158.9 us)
+  const int round = 4 * res * device_cu_count();
   const int wg_per_unit_max = (tiles_per_unit + 3) / 4;
   const int wg_per_unit = std::max(1, std::min(wg_per_unit_max, round / std::max(1, units)));
   const int tpw = (tiles_per_unit + 4 * wg_per_unit - 1) / (4 * wg_per_unit);
