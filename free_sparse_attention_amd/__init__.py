@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     cfg,
     dense_decode_attn,
     dense_decode_workspace_bytes,
+    describe_step,
     dims,
     import_kv_plain,
     load,

@@ -22,7 +22,7 @@ EXPORTED = (
     "fsa_last_error", "fsa_import_kv_plain", "fsa_append_kv", "fsa_build_page_meta", "fsa_meta_bytes",
     "fsa_quest_scores", "fsa_max_work_items", "fsa_select_pages",
     "fsa_sparse_decode_workspace_bytes", "fsa_sparse_decode_attn",
-    "fsa_dense_decode_workspace_bytes", "fsa_dense_decode_attn", "fsa_validate_inputs",
+    "fsa_dense_decode_workspace_bytes", "fsa_dense_decode_attn", "fsa_validate_inputs", "fsa_describe_step",
 )
 
 
@@ -73,6 +73,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             "fsa_dense_decode_workspace_bytes": (sz, [D, i32]),
             "fsa_dense_decode_attn": (i32, [D, f32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "fsa_validate_inputs": (i32, [D, i32, vp, vp, vp, vp, vp]),
+            "fsa_describe_step": (i32, [D, C, i32, ctypes.POINTER(i32), i32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -146,6 +147,21 @@ def meta_bytes(d: Dims) -> int:
 def quest_scores(d: Dims, c: LayerCfg, max_seq_len, q, meta, seq_lens, scores, stream=None):
     _check(load().fsa_quest_scores(ctypes.byref(d), c, int(max_seq_len), _p(q, "q", 2), _p(meta, "meta", 2),
                                    _i32(seq_lens, "seq_lens"), _p(scores, "scores", 4), _stream(stream)))
+
+
+STEP_INFO = ("plan", "replicas", "per_replica", "xcd_grouped", "prefetch", "pw_workgroups", "slots", "select_cols")
+PLANS = {0: "dense", 1: "wide", 2: "narrow"}
+
+
+def describe_step(d: Dims, c: LayerCfg, max_seq_len) -> dict:
+    """How the sparse step of these shapes runs on the current device (host only)."""
+    buf = (ctypes.c_int32 * len(STEP_INFO))()
+    n = load().fsa_describe_step(ctypes.byref(d), c, int(max_seq_len), buf, len(STEP_INFO))
+    if n < 0:
+        raise FsaError(FSA_ERR_INVALID_ARG, load().fsa_last_error().decode())
+    r = {k: int(buf[i]) for i, k in enumerate(STEP_INFO[:n])}
+    r["plan"] = PLANS[r["plan"]]
+    return r
 
 
 def max_work_items(d: Dims, c: LayerCfg, max_seq_len) -> int:

@@ -388,6 +388,27 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
   return hip_status(fsa::launch_attention(fsa::kList, w.plan, a, st), "decode attention launch");
 }
 
+int32_t fsa_describe_step(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len, int32_t* info,
+                          int32_t n_info) {
+  if (check_dims(dims) != FSA_OK || check_cfg(cfg) != FSA_OK || check_len(dims, max_seq_len) != FSA_OK) return -1;
+  if (!info || n_info < 0) {
+    fail(FSA_ERR_INVALID_ARG, "info must be non-null and n_info >= 0");
+    return -1;
+  }
+  const SparseWs w = sparse_ws(dims, cfg, max_seq_len);
+  const int32_t v[8] = {w.all_taken ? 0 : (w.step.sel_rep > 0 ? 1 : 2),
+                        w.step.sel_rep,
+                        w.step.sel_rep > 0 ? w.step.per : 0,
+                        w.step.xcd_grouped,
+                        w.step.prefetch,
+                        w.all_taken ? 0 : w.step.pw.wg_per_unit,
+                        w.slots,
+                        fsa::select_columns(max_seq_len)};
+  const int32_t n = std::min<int32_t>(n_info, 8);
+  for (int32_t i = 0; i < n; ++i) info[i] = v[i];
+  return n;
+}
+
 size_t fsa_dense_decode_workspace_bytes(const fsa_dims* dims, int32_t max_seq_len) {
   if (check_dims(dims) != FSA_OK || check_len(dims, max_seq_len) != FSA_OK) return 0;
   return dense_ws(dims, max_seq_len).total;

@@ -136,6 +136,7 @@ hipError_t launch_select_pages(const float* scores, const int32_t* page_table,
 
 // Largest candidate count one selection workgroup holds.
 int select_max_candidates();
+int select_columns(int max_seq_len);  // pages per selection thread for this length bound
 
 struct AttnPlan {
   int items_per_wave;  // work items each wave walks through

@@ -217,6 +217,7 @@ __global__ __launch_bounds__(kSelThreads) void select_attend_kernel(const StepAr
 }  // namespace
 
 int select_max_candidates() { return kSelMaxPages; }
+int select_columns(int max_seq_len) { return select_cols(max_seq_len); }
 
 hipError_t launch_select_pages(const float* scores, const int32_t* page_table,
                                const int32_t* seq_lens, int32_t* sel_pages, int32_t* work,

@@ -174,6 +174,23 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
                                   const int32_t* seq_lens, void* out, int32_t* sel_pages,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* How fsa_sparse_decode_attn will run a step of these shapes on the current
+ * device (host only: no device memory is touched; queries the device's
+ * compute-unit count, 256 when there is no device).  Writes up to n_info of:
+ *   info[0]  plan: 0 = every candidate fits the budget (dense kernels),
+ *            1 = wide (selection replicas attend the selected pages),
+ *            2 = narrow (one selection per unit, split-K launch)
+ *   info[1]  selection replicas per (b, KV head) unit (wide plan), else 0
+ *   info[2]  selected items each replica attends (wide plan), else 0
+ *   info[3]  1 if a unit's replicas are placed on one XCD
+ *   info[4]  1 if the replicas prefetch known-taken pages into that L2
+ *   info[5]  prefix/window workgroups per unit
+ *   info[6]  partial slots per unit (merged by the combine)
+ *   info[7]  pages per selection thread (a power of two)
+ * Returns the number of entries written, or -1 with fsa_last_error() set. */
+int32_t fsa_describe_step(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len, int32_t* info,
+                          int32_t n_info);
+
 /* Workspace (device bytes) that fsa_dense_decode_attn needs. */
 size_t fsa_dense_decode_workspace_bytes(const fsa_dims* dims, int32_t max_seq_len);
 

@@ -84,3 +84,36 @@ def test_bad_cfg_len_and_pointers(lib):
     assert lib.fsa_validate_inputs(ctypes.byref(d), 4096, p, p, p, None, None) == _lib.FSA_ERR_INVALID_ARG
     assert b"scratch" in lib.fsa_last_error()
     assert lib.fsa_validate_inputs(ctypes.byref(d), 0, p, p, p, p, None) == _lib.FSA_ERR_INVALID_ARG
+
+
+def _plan(B, hq, hkv, D, L, P, W, budget):
+    n = (L + 15) // 16 + 8
+    return fsa.describe_step(fsa.dims(B, hq, hkv, D, n, B * n), fsa.cfg(P, W, budget), L)
+
+
+def test_step_plans_on_256_cus(lib):
+    """Host-side planning (no device here: the library assumes MI355X's 256
+    CUs).  Shapes of the 64k, 256k and ragged serving workloads, a short
+    context and a many-replica case."""
+    p = _plan(4, 16, 4, 128, 65536, 128, 1024, 128)
+    assert (p["plan"], p["replicas"], p["per_replica"], p["xcd_grouped"], p["prefetch"], p["select_cols"]) == \
+        ("wide", 8, 16, 1, 1, 4)
+    assert p["slots"] == p["pw_workgroups"] + p["replicas"]
+    p = _plan(4, 32, 4, 128, 262144, 128, 4096, 256)  # one XCD's share of selected K/V (4 MiB) > half its L2
+    assert (p["plan"], p["replicas"], p["per_replica"], p["xcd_grouped"], p["prefetch"], p["select_cols"]) == \
+        ("wide", 8, 32, 1, 0, 16)
+    p = _plan(16, 32, 8, 128, 262144, 128, 2048, 256)  # 128 units: replicas would not fit
+    assert (p["plan"], p["replicas"], p["xcd_grouped"], p["prefetch"]) == ("narrow", 0, 0, 0)
+    p = _plan(9, 8, 1, 64, 6400, 32, 256, 224)  # 9 x 14 replicas fit, but 28 per XCD do not fit half an XCD
+    assert (p["plan"], p["replicas"], p["xcd_grouped"], p["prefetch"]) == ("wide", 14, 0, 0)
+    p = _plan(4, 16, 4, 128, 2048, 128, 1024, 128)  # every candidate fits the budget
+    assert p["plan"] == "dense" and p["replicas"] == 0
+    assert _plan(1, 8, 1, 128, 400001, 128, 4096, 256)["select_cols"] == 32
+
+
+def test_describe_step_rejects_bad_arguments(lib):
+    d = fsa.dims(1, 8, 2, 64, 100, 100)
+    buf = (ctypes.c_int32 * 8)()
+    assert lib.fsa_describe_step(ctypes.byref(d), fsa.cfg(16, 64, 4), 1600, None, 8) == -1
+    assert lib.fsa_describe_step(ctypes.byref(d), fsa.cfg(16, 64, 4), 1600, buf, 3) == 3
+    assert lib.fsa_describe_step(ctypes.byref(d), fsa.cfg(16, 64, 4), 10 ** 9, buf, 8) == -1

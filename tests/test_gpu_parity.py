@@ -18,6 +18,7 @@ import numpy as np
 import pytest
 import torch
 
+import free_sparse_attention_amd as fsa
 import oracle
 import synth
 from tests.gpu_harness import DeviceWorkload, bf16_f64, bits, to_dev_bf16
@@ -173,6 +174,20 @@ def test_many_units_both_step_plans(budget):
                                seq_lens=(4000, 2500, 3333, 1900, 4096, 3000, 2222, 3900), prefix=48, window=300,
                                budget=budget, k_sigma=0.5, n_needles=4, permuted=True)
     run_and_check(wl, units=[(0, 0), (1, 7), (4, 3), (7, 5), (2, 2)])
+
+
+def test_wide_plan_replicas_spread_over_xcds():
+    """9 units with budget 224: 14 selection replicas per unit (one selected
+    page per wave) fit on half the CUs, but two units' replicas per XCD (28)
+    would not fit in half an XCD, so the replicas are not grouped by XCD and
+    do not prefetch; the other wide-plan cases group them."""
+    wl = synth.workloads.build(name="spread", seed=20, batch=9, hq=8, hkv=1, d=64,
+                               seq_lens=(6000, 5100, 4700, 6400, 3900, 5555, 6100, 4400, 5000), prefix=32,
+                               window=256, budget=224, k_sigma=0.5, n_needles=4, permuted=True)
+    plan = fsa.describe_step(fsa.dims(wl.batch, wl.hq, wl.hkv, wl.d, wl.max_pages, wl.pool_pages), fsa.cfg(*wl.cfg),
+                             int(wl.seq_lens.max()))
+    assert (plan["plan"], plan["replicas"], plan["xcd_grouped"]) == ("wide", 14, 0), plan
+    run_and_check(wl, units=[(0, 0), (3, 0), (8, 0)])
 
 
 def test_longest_contexts_32_pages_per_thread():
