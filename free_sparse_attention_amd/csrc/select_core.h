@@ -1,7 +1,7 @@
 // Exact top-k page selection of one (sequence, KV head) by a 1024-thread
 // workgroup, and the merge of the selection with the pinned prefix and the
 // sliding window into a work list.  Used by the stand-alone selection kernel
-// and by the fused scoring + selection kernel.
+// and by the selection launch of the decode step.
 //
 // The paper (Abstract; analysis page "Methodology"; digest "The Move") keeps
 // a fixed budget of query-aware top-k pages next to the prefix and the
@@ -67,7 +67,6 @@ struct SelectJob {  // every optional field defaults to null / zero
   const float* scores = nullptr;     // the unit's scores, logical page p at [p]
   const int32_t* pt = nullptr;       // the sequence's page-table row
   const int32_t* seq_len = nullptr;  // the sequence's length (device)
-  const uint32_t* minmax = nullptr;  // (max key, ~min key) of the candidates, or null: computed here
   int max_seq_len = 0;
   int prefix = 0, window = 0, budget = 0, max_items = 0;
   int32_t* work = nullptr;    // the unit's work list, or null
@@ -177,11 +176,6 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
         (const __attribute__((address_space(1))) void*)(reinterpret_cast<const char*>(J.pt) + off),
         (__attribute__((address_space(3))) void*)(S.sphys + kSelThreads * j + kWave * wave), 4, 0, 0);
   }
-  uint32_t mm_in0 = 0, mm_in1 = 0;
-  if (J.minmax) {
-    mm_in0 = J.minmax[0];
-    mm_in1 = J.minmax[1];
-  }
   const int L = min(*J.seq_len, J.max_seq_len);  // lengths beyond the host bound are clamped
   const int Pe = min(J.prefix, L), Ws = max(0, L - J.window);
   const int c_lo = Pe / kPage;
@@ -215,22 +209,15 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
   if (radix) {
     need = (uint32_t)k;
     for (int i = tid; i < kSelBins; i += kSelThreads) S.hist[0][i] = 0;
-    uint32_t gmin, gmax;
-    if (J.minmax) {
-      gmax = mm_in0;
-      gmin = ~mm_in1;
-      __syncthreads();
-    } else {
-      kmin = wave_min(kmin);
-      kmax = wave_max(kmax);
-      if (lane == 0) {
-        S.mm[2 * wave] = kmin;
-        S.mm[2 * wave + 1] = kmax;
-      }
-      __syncthreads();
-      gmin = wave_min(lane < kSelWaves ? S.mm[2 * lane] : 0xFFFFFFFFu);
-      gmax = wave_max(lane < kSelWaves ? S.mm[2 * lane + 1] : 0u);
+    kmin = wave_min(kmin);
+    kmax = wave_max(kmax);
+    if (lane == 0) {
+      S.mm[2 * wave] = kmin;
+      S.mm[2 * wave + 1] = kmax;
     }
+    __syncthreads();
+    const uint32_t gmin = wave_min(lane < kSelWaves ? S.mm[2 * lane] : 0xFFFFFFFFu);
+    const uint32_t gmax = wave_max(lane < kSelWaves ? S.mm[2 * lane + 1] : 0u);
     if (gmin == gmax) {
       kprefix = gmin;  // every candidate ties: the lowest ids win
     } else {

@@ -4,15 +4,20 @@
 // Stand-alone: one 1024-thread workgroup per (sequence, KV head) selects and
 // writes the full work list (prefix, selected and window items).
 //
-// In the decode step the selection occupies one CU per (sequence, KV head)
-// for a few microseconds and needs little memory bandwidth, while the prefix
-// and window pages -- attended whatever the selection decides -- are known
-// from the sequence length alone.  So the same launch carries further
-// 1024-thread workgroups that attend the prefix and window pages on the other
-// CUs (16 waves, each walking a few pages with the flash-decoding of
-// attend_core.h, merged through LDS into one partial per workgroup).  The
-// selection then writes only the selected items, which the split-K attention
-// kernel attends next; the combine merges both kinds of partials.
+// In the decode step the selection occupies a CU for a few microseconds and
+// needs little memory bandwidth, while the prefix and window pages -- attended
+// whatever the selection decides -- are known from the sequence length alone.
+// So the selection launch also carries 1024-thread workgroups that attend the
+// prefix and window pages on the other CUs (16 waves, each walking a few pages
+// with the flash-decoding of attend_core.h, merged through LDS into one
+// partial per workgroup).  The selected pages are attended
+//   * wide plan: by the selection workgroups themselves -- sel_rep replicas
+//     per unit each run the (deterministic) selection and attend their own
+//     slice of the selected items; the replicas of a unit share one XCD and
+//     may prefetch pages already known to be taken into its L2;
+//   * narrow plan: by the split-K attention kernel launched next, from the
+//     selected items one selection workgroup per unit writes.
+// The combine merges all partials of a unit.
 #include <algorithm>
 
 #include "attend_core.h"
@@ -33,7 +38,6 @@ __global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
   J.scores = scores + (size_t)unit * max_pages;
   J.pt = page_table + (size_t)b * max_pages;
   J.seq_len = seq_lens + b;
-  J.minmax = nullptr;
   J.pf_kc = nullptr;
   J.max_seq_len = max_seq_len;
   J.prefix = prefix;
@@ -106,7 +110,6 @@ __device__ __forceinline__ SelectJob step_job(const StepArgs& A, int unit) {
   J.scores = A.scores + (size_t)unit * A.max_pages;
   J.pt = A.page_table + (size_t)b * A.max_pages;
   J.seq_len = A.seq_lens + b;
-  J.minmax = nullptr;
   J.pf_kc = nullptr;
   J.max_seq_len = A.max_seq_len;
   J.prefix = A.prefix;
