@@ -167,6 +167,7 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
 
   // ---- 1. scores, page-table entries and the length in one round trip
   // (page-table entries go straight to LDS: sphys[tid + 1024 j])
+  const int L_in = *J.seq_len;
   uint32_t key[COLS];
 #pragma unroll
   for (int j = 0; j < COLS; ++j) {
@@ -176,7 +177,15 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
         (const __attribute__((address_space(1))) void*)(reinterpret_cast<const char*>(J.pt) + off),
         (__attribute__((address_space(3))) void*)(S.sphys + kSelThreads * j + kWave * wave), 4, 0, 0);
   }
-  const int L = min(*J.seq_len, J.max_seq_len);  // lengths beyond the host bound are clamped
+  // Every load is issued before anything waits for one: while loads into LDS
+  // are pending the compiler can only wait for all loads, so a key used
+  // between two of them would cost a second round trip.
+  __builtin_amdgcn_sched_barrier(0);
+  // One explicit wait for all of it, on every path, so that the compiler
+  // knows no load into LDS is pending afterwards and adds no waits before
+  // later LDS accesses (which would also wait for the prefetch below).
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  const int L = min(L_in, J.max_seq_len);  // lengths beyond the host bound are clamped
   const int Pe = min(J.prefix, L), Ws = max(0, L - J.window);
   const int c_lo = Pe / kPage;
   const int c_hi = (Pe < Ws) ? (Ws + kPage - 1) / kPage : c_lo;  // candidates: pages [c_lo, c_hi)
@@ -204,7 +213,6 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
   uint32_t kprefix = 0, need = 0;
   int shift = 0;
   uint32_t pf[kPrefetch] = {0u, 0u, 0u, 0u};
-  bool pt_landed = false;  // this wave has waited for its page-table entries
   bool done = false;  // the threshold's bin holds exactly the keys still needed
   if (radix) {
     need = (uint32_t)k;
@@ -228,13 +236,17 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
         uint32_t* h_next = S.hist[(pass + 1) & 1];
         const int width = min(kSelDigitBits, top + 1);
         shift = top + 1 - width;
+        const uint32_t above = shift + width;  // <= 32: the bits above the digit
 #pragma unroll
         for (int j = 0; j < COLS; ++j) {
-          const uint32_t d = key[j] >> shift;  // shift + width <= 32, so d >> width is defined
+          // bit-field extracts: the key's bits above the digit (none when
+          // above == 32) and the digit itself, one instruction each
+          const uint32_t hi = __builtin_amdgcn_ubfe(key[j], above, 32u - above);
+          const uint32_t digit = __builtin_amdgcn_ubfe(key[j], (uint32_t)shift, (uint32_t)width);
           // every lane adds: pages outside the digit's range go to the lane's discard
           // slot, so the loop has no per-page branch
-          const bool in = ((cand >> j) & 1u) && (d >> width) == kprefix;
-          atomicAdd(&h[in ? (d & ((1u << width) - 1u)) : kSelBins + lane], 1u);
+          const bool in = ((cand >> j) & 1u) && hi == kprefix;
+          atomicAdd(&h[in ? digit : kSelBins + lane], 1u);
         }
         for (int i = tid; i < kSelBins; i += kSelThreads) h_next[i] = 0;  // for the next pass
         __syncthreads();
@@ -271,8 +283,6 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
         need = S.s_need;
         done = S.s_done;
         if (pass == 0 && J.pf_kc) {
-          __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's page-table entries are in LDS
-          pt_landed = true;
           prefetch_taken<COLS>(S, J, key, cand, shift, kprefix, done, tid, lane, pf);
         }
         if (done || shift == 0) break;
@@ -322,9 +332,6 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
     wc = lane == j ? (uint32_t)__popcll(g) : wc;
   }
   if (lane < COLS) S.cnt[1][lane * kSelWaves + wave] = wc;
-  // this wave's page-table entries have landed in LDS (after a prefetch this
-  // was waited for already; waiting again would wait for the prefetch)
-  if (!pt_landed) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   const uint32_t P = wave_word_prefix(S.cnt[1], nwords, wave, lane);
   int32_t* selw = J.sel_work ? J.sel_work : (J.work ? J.work + 4 * n_pre : nullptr);  // item o of the selection
