@@ -169,28 +169,38 @@ __device__ __forceinline__ void merge_waves(MergeLds<D, WAVES>& S, const WaveAtt
 #pragma unroll
       for (int r = 0; r < 4; ++r) S.o[wave][16 * t + 4 * gq + r][col] = st.acc[t][r];
   __syncthreads();
-  // per head: the maximum, the waves' weights and the weighted sum, once
-  if (threadIdx.x < 16) {
-    const int h = threadIdx.x;
-    float mw[WAVES], lw[WAVES];  // all reads first, so they are in flight together
+  // per head: the maximum, the waves' weights and the weighted sum, by wave 0:
+  // lane (part, h) takes waves part * WAVES/4 .. +WAVES/4 of head h, and the
+  // four parts of a head combine with two lane exchanges
+  static_assert(WAVES % 4 == 0, "the weights step splits the waves in four parts");
+  if (wave == 0) {
+    constexpr int PER = WAVES / 4;
+    const int h = lane & 15, part = lane >> 4;
+    float mw[PER], lw[PER];  // all reads first, so they are in flight together
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) {
-      mw[w] = S.m[w][h];
-      lw[w] = S.l[w][h];
+    for (int i = 0; i < PER; ++i) {
+      mw[i] = S.m[part * PER + i][h];
+      lw[i] = S.l[part * PER + i][h];
     }
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mw[w]);
+    for (int i = 0; i < PER; ++i) M = fmaxf(M, mw[i]);
+    M = fmaxf(M, __shfl_xor(M, 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
     float l = 0.f;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) {
-      mw[w] = mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - M);
-      l += mw[w] * lw[w];
+    for (int i = 0; i < PER; ++i) {
+      mw[i] = mw[i] == -INFINITY ? 0.f : exp2f(mw[i] - M);
+      l += mw[i] * lw[i];
     }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) S.e[w][h] = mw[w];
-    S.M[h] = M;
-    S.L[h] = l;
+    for (int i = 0; i < PER; ++i) S.e[part * PER + i][h] = mw[i];
+    if (part == 0) {
+      S.M[h] = M;
+      S.L[h] = l;
+    }
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < G * D; idx += WAVES * kWave) {
