@@ -190,6 +190,37 @@ def test_wide_plan_replicas_spread_over_xcds():
     run_and_check(wl, units=[(0, 0), (3, 0), (8, 0)])
 
 
+def _random_case(case):
+    rng = np.random.default_rng(1000 + case)
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8, 16]))
+    batch = int(rng.integers(1, 17))
+    lmax = int(rng.choice([3000, 40000]))
+    prefix = int(rng.choice([0, 16, 64, 128, 300]))
+    window = int(rng.choice([0, 64, 256, 1024, 5000]))
+    budget = int(rng.choice([0, 1, 7, 32, 128, 300]))
+    if case >= 10:  # many units with a large budget: the narrow plan
+        hkv, hq, batch, lmax, budget = 8, 8 * int(rng.choice([1, 2])), 12 + case % 5, 40000, 300
+    if prefix == window == budget == 0:
+        budget = 4
+    lens = tuple(int(x) for x in rng.integers(1, lmax, size=batch))
+    return dict(d=d, hq=hq, hkv=hkv, batch=batch, seq_lens=lens, prefix=prefix, window=window, budget=budget)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_shapes(case):
+    """Shapes, lengths and layer configurations drawn from a fixed seed per
+    case (batch 1-16, group 1-16, D 64/128, lengths up to 40k, prefix, window
+    and budget from empty to beyond the sequence); each step is checked
+    against the oracle on two units.  The cases cover the dense, wide and
+    narrow step plans."""
+    c = _random_case(case)
+    wl = synth.workloads.build(name=f"random{case}", seed=500 + case, k_sigma=0.5, n_needles=2,
+                               permuted=bool(case % 2), **c)
+    run_and_check(wl, units=[(0, 0), (c["batch"] - 1, c["hkv"] - 1)], dense=False)
+
+
 def test_longest_contexts_32_pages_per_thread():
     """Over 16384 pages (256k tokens) the selection holds 32 pages per thread."""
     wl = synth.workloads.build(name="long", seed=19, batch=1, hq=8, hkv=1, d=128, seq_lens=(400001,), prefix=128,
