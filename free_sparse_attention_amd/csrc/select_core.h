@@ -82,6 +82,7 @@ struct SelectJob {  // every optional field defaults to null / zero
   const uint16_t* pf_kc = nullptr;
   const uint16_t* pf_vc = nullptr;
   size_t pf_head_off = 0, pf_page_stride = 0;
+  int pf_lines = 0;  // 128-byte lines in one page's K block (and in its V block): head_dim / 4
   int pf_rep = 1, pf_r = 0;
 };
 
@@ -119,8 +120,8 @@ __device__ __forceinline__ uint32_t wave_word_prefix(const uint32_t* cnt, int nw
 // and V blocks requested into L2.  The pages are split over the pf_rep
 // workgroups by lane (lane mod pf_rep == pf_r); each such lane offers its first
 // known-taken page, and the wave fetches the first kPrefetch pages offered,
-// one load instruction per page: lanes 0-31 touch the 32 128-byte lines of the
-// K block, lanes 32-63 those of the V block.  The loaded words are returned so
+// one load instruction per page: one lane per 128-byte line of the page's K
+// block and of its V block (D / 4 lines each).  The loaded words are returned so
 // that the caller keeps them live (and so waits for them) only where it waits
 // for later loads anyway.
 template <int COLS>
@@ -138,13 +139,16 @@ __device__ __forceinline__ void prefetch_taken(const SelectLds& S, const SelectJ
   const int j0 = taken ? __builtin_ctz(taken) : 0;
   const int phys = S.sphys[tid + kSelThreads * j0];
   unsigned long long m = __ballot(taken != 0);
-  const uint16_t* base = (lane < 32 ? J.pf_kc : J.pf_vc) + J.pf_head_off + (size_t)(lane & 31) * 64;
+  // lanes [0, nl) touch the K block's lines, [nl, 2 nl) the V block's, the rest nothing
+  const int nl = J.pf_lines;
+  const bool toucher = lane < 2 * nl;
+  const uint16_t* base = (lane < nl ? J.pf_kc : J.pf_vc) + J.pf_head_off + (size_t)(lane & (nl - 1)) * 64;
 #pragma unroll
   for (int i = 0; i < kPrefetch; ++i) {
     if (m) {
       const int pp = __builtin_amdgcn_readlane(phys, __builtin_ctzll(m));
       m &= m - 1;
-      pf[i] = *reinterpret_cast<const uint32_t*>(base + (size_t)pp * J.pf_page_stride);
+      if (toucher) pf[i] = *reinterpret_cast<const uint32_t*>(base + (size_t)pp * J.pf_page_stride);
     }
   }
 }

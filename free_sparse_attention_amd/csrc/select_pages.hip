@@ -151,6 +151,7 @@ __device__ __forceinline__ void select_and_attend(SelectLds& SL, MergeLds<D, kSe
     J.pf_vc = A.vc;
     J.pf_head_off = (size_t)g * (kPage * D);
     J.pf_page_stride = (size_t)A.hkv * (kPage * D);
+    J.pf_lines = kPage * D * 2 / 128;
     J.pf_rep = A.sel_rep;
     J.pf_r = r;
   }
