@@ -342,16 +342,17 @@ def calibrate(steps, warmup):
 def layers12(steps, warmup):
     """One decode step of a 12-layer model at 128k context: for each layer (its
     own KV cache, metadata and per-layer prefix/window/budget of the 12-layer
-    sweep), append the new token's K/V and run the sparse decode.  Timed as
-    eager launches and as a captured HIP graph of two model steps (the
-    sequence lengths ping-pong between two buffers)."""
+    sweep), append the new token's K/V and run the sparse decode (one combined
+    call).  Timed as eager launches, as eager launches of the two separate
+    calls, and as a captured HIP graph of two model steps (the sequence
+    lengths ping-pong between two buffers)."""
     import torch
 
     import free_sparse_attention_amd as fsa
     import synth
     from tests.gpu_harness import DeviceWorkload, to_dev_bf16
 
-    extra = 2 * (warmup + steps) + 16
+    extra = 2 * (warmup + 2 * steps) + 16
     layers = []
     for l in range(12):
         wl = synth.make_workload("sweep12", layer=l, extra_tokens=extra)
@@ -365,25 +366,34 @@ def layers12(steps, warmup):
     outs = [torch.empty((wl0.batch, wl0.hq, wl0.d), dtype=torch.bfloat16, device="cuda") for _ in layers]
     wss = [dw.workspace(max_seq_len=msl) for dw in layers]
 
-    def model_step(i, stream):
+    def model_step(i, stream, combined=True):
         a, b = lens[i % 2], lens[(i + 1) % 2]
         for dw, out, ws in zip(layers, outs, wss):
-            fsa.append_kv(dw.dims, 1, kn, vn, dw.page_table, a, b, dw.k_cache, dw.v_cache, dw.meta, stream)
-            fsa.sparse_decode_attn(dw.dims, dw.cfg(), dw.wl.sm_scale, msl, dw.q, dw.k_cache, dw.v_cache, dw.meta,
-                                   dw.page_table, b, out, None, ws, stream)
+            if combined:  # one call: the append rides in the scoring launch when it can
+                fsa.append_decode_attn(dw.dims, 1, kn, vn, a, b, dw.cfg(), dw.wl.sm_scale, msl, dw.q, dw.k_cache,
+                                       dw.v_cache, dw.meta, dw.page_table, out, None, ws, stream)
+            else:
+                fsa.append_kv(dw.dims, 1, kn, vn, dw.page_table, a, b, dw.k_cache, dw.v_cache, dw.meta, stream)
+                fsa.sparse_decode_attn(dw.dims, dw.cfg(), dw.wl.sm_scale, msl, dw.q, dw.k_cache, dw.v_cache,
+                                       dw.meta, dw.page_table, b, out, None, ws, stream)
 
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def eager(first, combined):
+        e0.record(stream)
+        for i in range(steps):
+            model_step(first + i, stream, combined)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return 1000.0 * e0.elapsed_time(e1) / steps
+
     for i in range(warmup):
         model_step(i, stream)
     torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(steps):
-        model_step(warmup + i, stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    eager_us = 1000.0 * e0.elapsed_time(e1) / steps
-    done = warmup + steps  # even, so lens[0] holds the current lengths again
+    eager_us = eager(warmup, True)
+    separate_us = eager(warmup + steps, False)
+    done = warmup + 2 * steps  # even, so lens[0] holds the current lengths again
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         model_step(0, torch.cuda.current_stream())
@@ -401,22 +411,24 @@ def layers12(steps, warmup):
     torch.cuda.empty_cache()
     return {"layers": 12, "seq_len": int(wl0.seq_lens.max()), "eager_us_per_model_step": eager_us,
             "graph_us_per_model_step": graph_us, "eager_us_per_layer": eager_us / 12,
-            "graph_us_per_layer": graph_us / 12}
+            "graph_us_per_layer": graph_us / 12, "separate_calls_eager_us_per_model_step": separate_us}
 
 
 def ragged_serving(steps, warmup):
     """The 16-sequence serving batch (lengths 16k..256k, Hq 32 / Hkv 8, D 128,
     prefix 128, window 2048, budget 256, one shared permuted pool): a step is
-    one-token append to every sequence followed by the sparse decode."""
+    one-token append to every sequence followed by the sparse decode, as one
+    combined call (also timed as the two separate calls)."""
     import torch
 
     import free_sparse_attention_amd as fsa
     import synth
     from tests.gpu_harness import DeviceWorkload, to_dev_bf16
 
-    wl = synth.make_workload("ragged16", extra_tokens=2 * (warmup + steps) + 16)
+    extra = 3 * (warmup + steps) + 16
+    wl = synth.make_workload("ragged16", extra_tokens=extra)
     dw = DeviceWorkload(wl)
-    msl = int(wl.seq_lens.max()) + 2 * (warmup + steps) + 16
+    msl = int(wl.seq_lens.max()) + extra
     lens = [dw.seq_lens.clone(), torch.empty_like(dw.seq_lens)]
     kn = to_dev_bf16(np.zeros((wl.batch, 1, wl.hkv, wl.d), np.uint16) + 0x3F80)
     vn = kn.clone()
@@ -425,7 +437,12 @@ def ragged_serving(steps, warmup):
     c = dw.cfg()
     stream = torch.cuda.current_stream()
 
-    def step(i):
+    def step(i):  # one combined call: the append rides in the scoring launch
+        a, b = lens[i % 2], lens[(i + 1) % 2]
+        fsa.append_decode_attn(dw.dims, 1, kn, vn, a, b, c, wl.sm_scale, msl, dw.q, dw.k_cache, dw.v_cache, dw.meta,
+                               dw.page_table, out, None, ws, stream)
+
+    def separate_step(i):
         a, b = lens[i % 2], lens[(i + 1) % 2]
         fsa.append_kv(dw.dims, 1, kn, vn, dw.page_table, a, b, dw.k_cache, dw.v_cache, dw.meta, stream)
         fsa.sparse_decode_attn(dw.dims, c, wl.sm_scale, msl, dw.q, dw.k_cache, dw.v_cache, dw.meta, dw.page_table,
@@ -448,12 +465,17 @@ def ragged_serving(steps, warmup):
         torch.cuda.synchronize()
         return 1000.0 * e0.elapsed_time(e1) / n
 
-    # the two step kinds each append `warmup + steps` tokens per sequence
+    # the three step kinds each append `warmup + steps` tokens per sequence
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     us = run(step, warmup, steps)
     n0 = warmup + steps
+    for i in range(warmup):
+        separate_step(n0 + i)
+    torch.cuda.synchronize()
+    separate_us = run(separate_step, n0 + warmup, steps)
+    n0 = 2 * (warmup + steps)
     for i in range(warmup):
         dense_step(n0 + i)
     torch.cuda.synchronize()
@@ -470,7 +492,8 @@ def ragged_serving(steps, warmup):
     torch.cuda.empty_cache()
     return {"sequences": wl.batch, "seq_len_min": int(L.min()), "seq_len_max": int(L.max()),
             "us_per_step": us, "steps_per_s": 1e6 / us, "step_alg_bytes": alg, "step_GBps": alg / us / 1e3,
-            "dense_us_per_step": dense_us, "speedup_vs_dense": dense_us / us}
+            "dense_us_per_step": dense_us, "speedup_vs_dense": dense_us / us,
+            "separate_calls_us_per_step": separate_us}
 
 
 def main():

@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     Dims,
     FsaError,
     LayerCfg,
+    append_decode_attn,
     append_kv,
     build_page_meta,
     cfg,

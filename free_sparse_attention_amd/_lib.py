@@ -23,6 +23,7 @@ EXPORTED = (
     "fsa_quest_scores", "fsa_max_work_items", "fsa_select_pages",
     "fsa_sparse_decode_workspace_bytes", "fsa_sparse_decode_attn",
     "fsa_dense_decode_workspace_bytes", "fsa_dense_decode_attn", "fsa_validate_inputs", "fsa_describe_step",
+    "fsa_append_decode_attn",
 )
 
 
@@ -74,6 +75,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             "fsa_dense_decode_attn": (i32, [D, f32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "fsa_validate_inputs": (i32, [D, i32, vp, vp, vp, vp, vp]),
             "fsa_describe_step": (i32, [D, C, i32, ctypes.POINTER(i32), i32]),
+            "fsa_append_decode_attn": (i32, [D, i32, vp, vp, vp, vp, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                             sz, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -193,6 +196,16 @@ def sparse_decode_attn(d: Dims, c: LayerCfg, sm_scale, max_seq_len, q, k_cache, 
         _p(v_cache, "v_cache", 2), _p(meta, "meta", 2), _i32(page_table, "page_table"),
         _i32(seq_lens, "seq_lens"), _p(out, "out", 2), _i32(sel_pages, "sel_pages"),
         _p(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def append_decode_attn(d: Dims, n_new, k_new, v_new, seq_lens, seq_lens_out, c: LayerCfg, sm_scale, max_seq_len,
+                       q, k_cache, v_cache, meta, page_table, out, sel_pages, workspace, stream=None):
+    _check(load().fsa_append_decode_attn(
+        ctypes.byref(d), int(n_new), _p(k_new, "k_new", 2), _p(v_new, "v_new", 2), _i32(seq_lens, "seq_lens"),
+        _i32(seq_lens_out, "seq_lens_out"), c, float(sm_scale), int(max_seq_len), _p(q, "q", 2),
+        _p(k_cache, "k_cache", 2), _p(v_cache, "v_cache", 2), _p(meta, "meta", 2), _i32(page_table, "page_table"),
+        _p(out, "out", 2), _i32(sel_pages, "sel_pages"), _p(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def dense_decode_workspace_bytes(d: Dims, max_seq_len) -> int:

@@ -7,7 +7,7 @@
 #include <string>
 
 #include "../../include/fsa.h"
-#include "fsa_internal.h"
+#include "append_core.h"
 
 namespace {
 
@@ -306,11 +306,13 @@ size_t fsa_sparse_decode_workspace_bytes(const fsa_dims* dims, fsa_layer_cfg cfg
   return sparse_ws(dims, cfg, max_seq_len).total;
 }
 
-fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_scale,
-                                  int32_t max_seq_len, const void* q, const void* k_cache,
-                                  const void* v_cache, const void* meta, const int32_t* page_table,
-                                  const int32_t* seq_lens, void* out, int32_t* sel_pages,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C" (reopened below)
+
+namespace {
+
+fsa_status check_step(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_scale, int32_t max_seq_len, const void* q,
+                      const void* k_cache, const void* v_cache, const void* meta, const int32_t* page_table,
+                      const int32_t* seq_lens, void* out, void* workspace, size_t workspace_bytes) {
   FSA_CHECK(check_dims(dims));
   FSA_CHECK(check_cfg(cfg));
   FSA_CHECK(check_len(dims, max_seq_len));
@@ -322,10 +324,30 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
   FSA_CHECK(need(seq_lens, "seq_lens"));
   FSA_CHECK(need(out, "out"));
   if (!(sm_scale > 0.f)) return fail(FSA_ERR_INVALID_ARG, "sm_scale must be > 0");
+  const size_t total = sparse_ws(dims, cfg, max_seq_len).total;
+  if (!workspace || workspace_bytes < total)
+    return fail(FSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, total);
+  return FSA_OK;
+}
+
+// The decode step over seq_lens.  With `append`, the step first appends its
+// tokens (seq_lens are then the lengths after the append, which it writes):
+// inside the scoring launch when that is safe, else as a launch of its own.
+fsa_status run_sparse_step(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_scale, int32_t max_seq_len,
+                           const void* q, const void* k_cache, const void* v_cache, const void* meta,
+                           const int32_t* page_table, const int32_t* seq_lens, void* out, int32_t* sel_pages,
+                           void* workspace, hipStream_t st, const fsa::AppendArgs* append) {
   const SparseWs w = sparse_ws(dims, cfg, max_seq_len);
-  if (!workspace || workspace_bytes < w.total)
-    return fail(FSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, w.total);
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  // The scoring launch carries the append when no page the append touches can
+  // be a candidate: the touched pages start at or after 16 floor(L0 / 16) and
+  // candidates end before L0 + n_new - window, so window >= n_new + 15 suffices.
+  const bool fused = append && !w.all_taken && cfg.window_tokens >= append->n_new + fsa::kPage - 1;
+  if (append && !fused)
+    FSA_CHECK(hip_status(fsa::launch_append_kv(append->n_new, append->k_new, append->v_new, append->page_table,
+                                               append->seq_lens, append->seq_lens_out, append->kc, append->vc,
+                                               append->meta, dims->batch, dims->num_kv_heads, dims->head_dim,
+                                               dims->max_pages_per_seq, st),
+                         "append_kv launch"));
   if (w.all_taken) {
     // every candidate page is selected: the attended set is [0, L), i.e. dense
     // attention; the selection runs only to report the selected pages (it
@@ -343,10 +365,10 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
   }
   FSA_CHECK(hip_status(
       fsa::launch_quest_scores(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(meta),
-                               seq_lens, at<float>(workspace, w.scores), dims->batch,
+                               fused ? append->seq_lens : seq_lens, at<float>(workspace, w.scores), dims->batch,
                                dims->num_q_heads, dims->num_kv_heads, dims->head_dim,
                                dims->max_pages_per_seq, cfg.prefix_tokens, cfg.window_tokens,
-                               max_seq_len, st),
+                               max_seq_len, st, fused ? append : nullptr),
       "quest_scores launch"));
   fsa::StepArgs sa;
   sa.scores = at<float>(workspace, w.scores);
@@ -386,6 +408,41 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
   a.slots_per_unit = w.slots;
   a.slot_base = w.step.pw.wg_per_unit;
   return hip_status(fsa::launch_attention(fsa::kList, w.plan, a, st), "decode attention launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_scale,
+                                  int32_t max_seq_len, const void* q, const void* k_cache,
+                                  const void* v_cache, const void* meta, const int32_t* page_table,
+                                  const int32_t* seq_lens, void* out, int32_t* sel_pages,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  FSA_CHECK(check_step(dims, cfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table, seq_lens, out,
+                       workspace, workspace_bytes));
+  return run_sparse_step(dims, cfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table, seq_lens, out,
+                         sel_pages, workspace, static_cast<hipStream_t>(stream), nullptr);
+}
+
+fsa_status fsa_append_decode_attn(const fsa_dims* dims, int32_t n_new, const void* k_new, const void* v_new,
+                                  const int32_t* seq_lens, int32_t* seq_lens_out, fsa_layer_cfg cfg,
+                                  float sm_scale, int32_t max_seq_len, const void* q, void* k_cache,
+                                  void* v_cache, void* meta, const int32_t* page_table, void* out,
+                                  int32_t* sel_pages, void* workspace, size_t workspace_bytes, void* stream) {
+  FSA_CHECK(check_step(dims, cfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table, seq_lens_out, out,
+                       workspace, workspace_bytes));
+  if (n_new < 1) return fail(FSA_ERR_INVALID_ARG, "n_new must be >= 1");
+  FSA_CHECK(need(k_new, "k_new"));
+  FSA_CHECK(need(v_new, "v_new"));
+  FSA_CHECK(need(seq_lens, "seq_lens"));
+  if (seq_lens_out == seq_lens) return fail(FSA_ERR_INVALID_ARG, "seq_lens_out must not alias seq_lens");
+  const fsa::AppendArgs a = fsa::append_args(
+      n_new, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), page_table, seq_lens,
+      seq_lens_out, static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), static_cast<uint16_t*>(meta),
+      dims->num_kv_heads, dims->max_pages_per_seq);
+  return run_sparse_step(dims, cfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table, seq_lens_out,
+                         out, sel_pages, workspace, static_cast<hipStream_t>(stream), &a);
 }
 
 int32_t fsa_describe_step(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len, int32_t* info,

@@ -124,9 +124,13 @@ hipError_t launch_build_page_meta(const uint16_t* kc, const int32_t* page_table,
                                   const int32_t* seq_lens, uint16_t* meta, int batch, int hkv,
                                   int d, int max_pages, int max_seq_len, hipStream_t stream);
 
+struct AppendArgs;
+// With `append` (combined append + decode step), the launch also performs the
+// append, and seq_lens are the lengths before it.
 hipError_t launch_quest_scores(const uint16_t* q, const uint16_t* meta, const int32_t* seq_lens,
                                float* scores, int batch, int hq, int hkv, int d, int max_pages,
-                               int prefix, int window, int max_seq_len, hipStream_t stream);
+                               int prefix, int window, int max_seq_len, hipStream_t stream,
+                               const AppendArgs* append = nullptr);
 
 hipError_t launch_select_pages(const float* scores, const int32_t* page_table,
                                const int32_t* seq_lens, int32_t* sel_pages, int32_t* work,

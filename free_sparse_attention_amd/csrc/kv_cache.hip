@@ -7,7 +7,7 @@
 // max are exact selections, so the kernels work on order-preserving 16-bit
 // integer keys of the bf16 bit patterns: no rounding, and the result does not
 // depend on the order in which tokens are combined.  A zero is written as +0.
-#include "fsa_internal.h"
+#include "append_core.h"
 
 namespace fsa {
 namespace {
@@ -43,116 +43,10 @@ __global__ __launch_bounds__(64) void import_kv_plain_kernel(const uint16_t* __r
   }
 }
 
-// Min/max keys of the 8 channels held by each lane, reduced over the 16 lanes
-// of the same chunk (lanes differ in token slot); `valid` masks slots out.
-__device__ __forceinline__ void chunk_minmax(const uint4& kv, bool valid, uint32_t mn[8],
-                                             uint32_t mx[8]) {
-  const uint32_t w[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t key = bf16_order_key((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-    mn[e] = valid ? key : 0xFFFFu;
-    mx[e] = valid ? key : 0u;
-  }
-#pragma unroll
-  for (int off = 1; off < kPage; off <<= 1) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      mn[e] = min(mn[e], (uint32_t)__shfl_xor((int)mn[e], off, kPage));
-      mx[e] = max(mx[e], (uint32_t)__shfl_xor((int)mx[e], off, kPage));
-    }
-  }
-}
-
-// Metadata of channel chunk c (channels 8c .. 8c + 7) of logical page p of unit u.
-__device__ __forceinline__ uint4* meta_min_chunk(uint16_t* meta, int u, int p, int c, int tiles, int D) {
-  return reinterpret_cast<uint4*>(meta + meta_offset(u, p, 8 * c, tiles, D));
-}
-__device__ __forceinline__ uint4* meta_max_chunk(uint16_t* meta, int u, int p, int c, int tiles, int D) {
-  return reinterpret_cast<uint4*>(meta + meta_offset(u, p, D + 8 * c, tiles, D));
-}
-
-__device__ __forceinline__ void store_meta_chunk(uint16_t* meta, int u, int p, int c, int tiles, int D,
-                                                 const uint32_t mn[8], const uint32_t mx[8]) {
-  uint32_t lo[4], hi[4];
-#pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    lo[e >> 1] = bf16_from_order_key(mn[e]) | (bf16_from_order_key(mn[e + 1]) << 16);
-    hi[e >> 1] = bf16_from_order_key(mx[e]) | (bf16_from_order_key(mx[e + 1]) << 16);
-  }
-  *meta_min_chunk(meta, u, p, c, tiles, D) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-  *meta_max_chunk(meta, u, p, c, tiles, D) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-}
-
-// One wave per (sequence, KV head, touched page).  Lane (slot = lane % 16,
-// chunk = 4 * it + lane / 16) moves one 16-byte chunk of one new token.
+// One wave per (sequence, KV head, touched page).
 template <int D>
-__global__ __launch_bounds__(64) void append_kv_kernel(
-    int n_new, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
-    int32_t* __restrict__ seq_lens_out, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
-    uint16_t* __restrict__ meta, int hkv, int max_pages, int touch) {
-  constexpr int NCH = D / 8;
-  const int unit = blockIdx.x / touch, j = blockIdx.x % touch;
-  const int b = unit / hkv, g = unit % hkv;
-  const int L0 = seq_lens[b];
-  const int lane = threadIdx.x, slot = lane % kPage;
-  if (seq_lens_out != nullptr && g == 0 && j == 0 && lane == 0) seq_lens_out[b] = L0 + n_new;
-  const int p = L0 / kPage + j;
-  if (p >= max_pages) return;  // positions past the page table are dropped
-  const int t_lo = max(L0, p * kPage), t_hi = min(L0 + n_new, p * kPage + kPage);
-  if (t_lo >= t_hi) return;
-  const int s0 = t_lo - p * kPage, s1 = t_hi - p * kPage;
-  const size_t blk = (size_t)page_table[(size_t)b * max_pages + p] * hkv + g;
-  const int tiles = meta_tiles(max_pages);
-  const bool valid = slot >= s0 && slot < s1;
-  const bool merge = slot == 0 && s0 > 0;  // the page already holds tokens: merge with its metadata
-  // Every load first (new tokens, old metadata; one round trip beside the
-  // page-table entry), every store after: on this target a load wait also
-  // waits for earlier stores.
-  constexpr int NIT = NCH / 4;
-  uint4 kv[NIT], vv[NIT], om[NIT], oM[NIT];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int c = 4 * it + lane / kPage;
-    kv[it] = vv[it] = om[it] = oM[it] = make_uint4(0, 0, 0, 0);
-    if (valid) {
-      const size_t src = (((size_t)b * n_new + (p * kPage + slot - L0)) * hkv + g) * D + c * 8;
-      kv[it] = *reinterpret_cast<const uint4*>(k_new + src);
-      vv[it] = *reinterpret_cast<const uint4*>(v_new + src);
-    }
-    if (merge) {
-      om[it] = *meta_min_chunk(meta, unit, p, c, tiles, D);
-      oM[it] = *meta_max_chunk(meta, unit, p, c, tiles, D);
-    }
-  }
-  uint16_t* kdst = kc + blk * (kPage * D);
-  uint16_t* vdst = vc + blk * (kPage * D);
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int c = 4 * it + lane / kPage;
-    if (valid) {
-      *reinterpret_cast<uint4*>(kdst + (c * kPage + slot) * 8) = kv[it];
-      const uint32_t w[4] = {vv[it].x, vv[it].y, vv[it].z, vv[it].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vdst[(c * 8 + e) * kPage + slot] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-    }
-    uint32_t mn[8], mx[8];
-    chunk_minmax(kv[it], valid, mn, mx);
-    if (slot == 0) {
-      if (merge) {
-        const uint32_t a[4] = {om[it].x, om[it].y, om[it].z, om[it].w};
-        const uint32_t z[4] = {oM[it].x, oM[it].y, oM[it].z, oM[it].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          mn[e] = min(mn[e], bf16_order_key((a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
-          mx[e] = max(mx[e], bf16_order_key((z[e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
-        }
-      }
-      store_meta_chunk(meta, unit, p, c, tiles, D, mn, mx);
-    }
-  }
+__global__ __launch_bounds__(64) void append_kv_kernel(const AppendArgs A) {
+  append_task<D>(A, blockIdx.x, threadIdx.x);
 }
 
 // One wave per (sequence, logical page, KV head) over pages in use.
@@ -201,14 +95,13 @@ hipError_t launch_append_kv(int n_new, const uint16_t* k_new, const uint16_t* v_
                             const int32_t* page_table, const int32_t* seq_lens,
                             int32_t* seq_lens_out, uint16_t* kc, uint16_t* vc, uint16_t* meta,
                             int batch, int hkv, int d, int max_pages, hipStream_t stream) {
-  const int touch = (n_new + kPage - 1) / kPage + 1;  // pages one append can reach
-  const dim3 grid((unsigned)((size_t)batch * hkv * touch));
+  const AppendArgs a = append_args(n_new, k_new, v_new, page_table, seq_lens, seq_lens_out, kc, vc, meta, hkv,
+                                   max_pages);
+  const dim3 grid((unsigned)((size_t)batch * hkv * a.touch));
   if (d == 128)
-    hipLaunchKernelGGL(append_kv_kernel<128>, grid, dim3(64), 0, stream, n_new, k_new, v_new,
-                       page_table, seq_lens, seq_lens_out, kc, vc, meta, hkv, max_pages, touch);
+    hipLaunchKernelGGL(append_kv_kernel<128>, grid, dim3(64), 0, stream, a);
   else
-    hipLaunchKernelGGL(append_kv_kernel<64>, grid, dim3(64), 0, stream, n_new, k_new, v_new,
-                       page_table, seq_lens, seq_lens_out, kc, vc, meta, hkv, max_pages, touch);
+    hipLaunchKernelGGL(append_kv_kernel<64>, grid, dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@
 #include <algorithm>
 #include <atomic>
 
-#include "fsa_internal.h"
+#include "append_core.h"
 
 namespace fsa {
 namespace {
@@ -43,15 +43,30 @@ __device__ __forceinline__ uint32_t keep_sign(uint32_t w, bool negative) {
 // the non-temporal hint: it is read once per step and should not displace
 // cached data (on MI355X this streams about a quarter faster at 256k tokens
 // than plain loads or a contiguous run of tiles per wave).
+//
+// In the combined append + decode step the same launch also carries the
+// append: its tasks (append_core.h) in the first append_blocks workgroups, one
+// per wave; the scoring then takes the lengths after the append (seq_lens +
+// len_add).  The host uses this only when no page the append touches can be a
+// candidate (window >= n_new + 15), so the two roles write and read disjoint
+// data; the scores of the touched pages' tiles that are not candidates are
+// computed from metadata being rewritten, but never stored.
 template <int D>
 __global__ __launch_bounds__(256) void quest_score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ meta,
     const int32_t* __restrict__ seq_lens, float* __restrict__ scores, int hq, int hkv,
-    int max_pages, int prefix, int window, int tiles_per_wave, int wg_per_unit, int max_seq_len) {
+    int max_pages, int prefix, int window, int tiles_per_wave, int wg_per_unit, int max_seq_len,
+    const AppendArgs ap, int append_blocks, int append_tasks, int len_add) {
   constexpr int NSTEP = 2 * D / 32;  // k-steps over the 2D metadata values
-  const int unit = blockIdx.x / wg_per_unit, wg = blockIdx.x % wg_per_unit;
-  const int b = unit / hkv, g = unit % hkv, G = hq / hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if ((int)blockIdx.x < append_blocks) {
+    const int w = (int)blockIdx.x * 4 + wave;
+    if (w < append_tasks) append_task<D>(ap, w, lane);
+    return;
+  }
+  const int blk = (int)blockIdx.x - append_blocks;
+  const int unit = blk / wg_per_unit, wg = blk % wg_per_unit;
+  const int b = unit / hkv, g = unit % hkv, G = hq / hkv;
   const int col = lane & 15, gq = lane >> 4;
   // Every sequence with candidates has L > prefix, so its candidates start at
   // page prefix / 16 and end at or before the host bound's: the wave's first
@@ -88,7 +103,7 @@ __global__ __launch_bounds__(256) void quest_score_kernel(
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) bufA[s] = ld_nt(reinterpret_cast<const uint4*>(src + s * (kMetaTile * 32)));
   }
-  const int L = min(seq_lens[b], max_seq_len);  // lengths beyond the host bound are clamped
+  const int L = min(seq_lens[b] + len_add, max_seq_len);  // lengths beyond the host bound are clamped
   const int Pe = min(prefix, L), Ws = max(0, L - window);
   if (Pe >= Ws) return;
   const int c_lo = Pe / kPage, c_hi = (Ws + kPage - 1) / kPage;  // c_lo == c_lo_h here
@@ -139,7 +154,8 @@ __global__ __launch_bounds__(256) void quest_score_kernel(
 
 hipError_t launch_quest_scores(const uint16_t* q, const uint16_t* meta, const int32_t* seq_lens,
                                float* scores, int batch, int hq, int hkv, int d, int max_pages,
-                               int prefix, int window, int max_seq_len, hipStream_t stream) {
+                               int prefix, int window, int max_seq_len, hipStream_t stream,
+                               const AppendArgs* append) {
   const int units = batch * hkv;
   const int max_cand = (max_seq_len + kPage - 1) / kPage;
   const int tiles_per_unit = (max_cand + kMetaTile - 1) / kMetaTile + 1;  // a range may straddle one more
@@ -159,13 +175,23 @@ hipError_t launch_quest_scores(const uint16_t* q, const uint16_t* meta, const in
   const int wg_per_unit_max = (tiles_per_unit + 3) / 4;
   const int wg_per_unit = std::max(1, std::min(wg_per_unit_max, round / std::max(1, units)));
   const int tpw = (tiles_per_unit + 4 * wg_per_unit - 1) / (4 * wg_per_unit);
-  const dim3 grid((unsigned)((long)units * wg_per_unit));
+  AppendArgs ap{};
+  int append_tasks = 0, len_add = 0;
+  if (append) {
+    ap = *append;
+    append_tasks = units * ap.touch;
+    len_add = ap.n_new;
+  }
+  const int append_blocks = (append_tasks + 3) / 4;
+  const dim3 grid((unsigned)((long)append_blocks + (long)units * wg_per_unit));
   if (d == 128)
     hipLaunchKernelGGL(quest_score_kernel<128>, grid, dim3(256), 0, stream, q, meta, seq_lens,
-                       scores, hq, hkv, max_pages, prefix, window, tpw, wg_per_unit, max_seq_len);
+                       scores, hq, hkv, max_pages, prefix, window, tpw, wg_per_unit, max_seq_len, ap,
+                       append_blocks, append_tasks, len_add);
   else
     hipLaunchKernelGGL(quest_score_kernel<64>, grid, dim3(256), 0, stream, q, meta, seq_lens,
-                       scores, hq, hkv, max_pages, prefix, window, tpw, wg_per_unit, max_seq_len);
+                       scores, hq, hkv, max_pages, prefix, window, tpw, wg_per_unit, max_seq_len, ap,
+                       append_blocks, append_tasks, len_add);
   return hipGetLastError();
 }
 

@@ -191,6 +191,25 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
 int32_t fsa_describe_step(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len, int32_t* info,
                           int32_t n_info);
 
+/* fsa_append_kv followed by fsa_sparse_decode_attn on the same stream, as one
+ * call: the decode step of a model that has just produced the new tokens'
+ * K/V.  Results (caches, metadata, seq_lens_out, out, sel_pages) equal those
+ * of the two calls bit for bit.  When no page the append writes can be a
+ * candidate of the step (window_tokens >= n_new + 15, and more candidates
+ * than the budget) the append runs inside the scoring launch, one launch
+ * fewer; otherwise it runs as its own launch first.
+ *   seq_lens      int32 [B] (device), lengths before the append
+ *   seq_lens_out  int32 [B] (device), receives seq_lens[b] + n_new: the
+ *                 lengths the decode step uses; must not alias seq_lens
+ *   max_seq_len   host upper bound on the lengths after the append
+ *   workspace     fsa_sparse_decode_workspace_bytes(dims, cfg, max_seq_len)
+ * Other arguments as in fsa_append_kv and fsa_sparse_decode_attn. */
+fsa_status fsa_append_decode_attn(const fsa_dims* dims, int32_t n_new, const void* k_new, const void* v_new,
+                                  const int32_t* seq_lens, int32_t* seq_lens_out, fsa_layer_cfg cfg,
+                                  float sm_scale, int32_t max_seq_len, const void* q, void* k_cache,
+                                  void* v_cache, void* meta, const int32_t* page_table, void* out,
+                                  int32_t* sel_pages, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace (device bytes) that fsa_dense_decode_attn needs. */
 size_t fsa_dense_decode_workspace_bytes(const fsa_dims* dims, int32_t max_seq_len);
 

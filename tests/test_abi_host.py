@@ -80,6 +80,17 @@ def test_bad_cfg_len_and_pointers(lib):
     assert st == _lib.FSA_ERR_INVALID_ARG
     st = lib.fsa_dense_decode_attn(ctypes.byref(d), 0.125, 4096, p, p, p, p, p, p, p, 0, None)
     assert st == _lib.FSA_ERR_WORKSPACE
+    # combined append + decode: the append's and the step's checks, before any launch
+    c = fsa.cfg(64, 256, 32)
+    assert lib.fsa_append_decode_attn(ctypes.byref(d), 0, p, p, p, p, c, 0.125, 4096, p, p, p, p, p, p, None, p, need,
+                                      None) == _lib.FSA_ERR_INVALID_ARG
+    assert lib.fsa_append_decode_attn(ctypes.byref(d), 1, p, p, p, p, c, 0.125, 4096, p, p, p, p, p, p, None, p, need,
+                                      None) == _lib.FSA_ERR_INVALID_ARG
+    assert b"alias" in lib.fsa_last_error()
+    assert lib.fsa_append_decode_attn(ctypes.byref(d), 1, p, p, p, None, c, 0.125, 4096, p, p, p, p, p, p, None, p,
+                                      need, None) == _lib.FSA_ERR_INVALID_ARG
+    assert lib.fsa_append_decode_attn(ctypes.byref(d), 1, p, p, p, ctypes.c_void_p(32), c, 0.125, 4096, p, p, p, p,
+                                      p, p, None, p, need - 1, None) == _lib.FSA_ERR_WORKSPACE
     # the validator checks its host arguments before any launch
     assert lib.fsa_validate_inputs(ctypes.byref(d), 4096, p, p, p, None, None) == _lib.FSA_ERR_INVALID_ARG
     assert b"scratch" in lib.fsa_last_error()

@@ -325,6 +325,48 @@ def test_append_matches_rebuild_and_oracle():
     run_and_check(wl, dw=dw)
 
 
+@pytest.mark.parametrize("cfg,chunks", [((128, 1024, 16), [1, 1, 37, 1, 16, 1]),  # append inside the scoring launch
+                                        ((32, 10, 8), [1, 5, 1, 7]),  # window < n_new + 15: append launched first
+                                        ((16, 4096, 64), [3, 1])])  # every candidate fits the budget: dense path
+def test_append_decode_equals_append_then_decode(cfg, chunks):
+    """fsa_append_decode_attn gives bit for bit the caches, metadata, lengths,
+    output and selection of fsa_append_kv followed by fsa_sparse_decode_attn,
+    step after step, with the append fused into the scoring launch or not."""
+    import free_sparse_attention_amd as fsa
+    wl = synth.workloads.build(name="appdec", seed=21, batch=3, hq=8, hkv=2, d=128, seq_lens=(3000, 1999, 4095),
+                               prefix=cfg[0], window=cfg[1], budget=cfg[2], k_sigma=0.5, permuted=True,
+                               extra_tokens=200)
+    a, b = DeviceWorkload(wl), DeviceWorkload(wl)
+    c = fsa.cfg(*cfg)
+    msl = int(wl.seq_lens.max()) + sum(chunks)
+    ws_a = torch.empty(fsa.sparse_decode_workspace_bytes(a.dims, c, msl), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty_like(ws_a)
+    la = [torch.from_numpy(wl.seq_lens.copy()).cuda(), torch.empty(wl.batch, dtype=torch.int32, device="cuda")]
+    lb = [la[0].clone(), torch.empty_like(la[1])]
+    out_a = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.bfloat16, device="cuda")
+    out_b = torch.empty_like(out_a)
+    sel_a = torch.full((wl.batch, wl.hkv, max(cfg[2], 1)), -7, dtype=torch.int32, device="cuda")
+    sel_b = torch.full_like(sel_a, -7)
+    L = wl.seq_lens.copy()
+    for step, n in enumerate(chunks):
+        say(f"[append_decode] cfg={cfg} step {step} n_new={n}")
+        kn, vn = _tokens_at(wl, L, n)
+        kn, vn = to_dev_bf16(kn), to_dev_bf16(vn)
+        fsa.append_kv(a.dims, n, kn, vn, a.page_table, la[0], la[1], a.k_cache, a.v_cache, a.meta)
+        fsa.sparse_decode_attn(a.dims, c, wl.sm_scale, msl, a.q, a.k_cache, a.v_cache, a.meta, a.page_table, la[1],
+                               out_a, sel_a, ws_a)
+        fsa.append_decode_attn(b.dims, n, kn, vn, lb[0], lb[1], c, wl.sm_scale, msl, b.q, b.k_cache, b.v_cache,
+                               b.meta, b.page_table, out_b, sel_b, ws_b)
+        torch.cuda.synchronize()
+        assert torch.equal(la[1], lb[1])
+        assert np.array_equal(bits(out_a), bits(out_b)), f"output, step {step}"
+        assert torch.equal(sel_a, sel_b), f"selection, step {step}"
+        assert torch.equal(a.meta, b.meta) and torch.equal(a.k_cache, b.k_cache) and torch.equal(a.v_cache, b.v_cache)
+        la.reverse()
+        lb.reverse()
+        L = L + n
+
+
 def _tokens_at(wl, lens, n):
     kk, kv, _ = wl.keys()
     kn = np.empty((wl.batch, n, wl.hkv, wl.d), np.uint16)
