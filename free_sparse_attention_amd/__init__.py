@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     cfg,
     dense_decode_attn,
     dense_decode_workspace_bytes,
+    device_memory,
     describe_step,
     dims,
     import_kv_plain,
@@ -22,6 +23,7 @@ from ._lib import (  # noqa: F401
     max_work_items,
     meta_bytes,
     quest_scores,
+    read_probe,
     select_pages,
     sparse_decode_attn,
     sparse_decode_workspace_bytes,

@@ -23,7 +23,7 @@ EXPORTED = (
     "fsa_quest_scores", "fsa_max_work_items", "fsa_select_pages",
     "fsa_sparse_decode_workspace_bytes", "fsa_sparse_decode_attn",
     "fsa_dense_decode_workspace_bytes", "fsa_dense_decode_attn", "fsa_validate_inputs", "fsa_describe_step",
-    "fsa_append_decode_attn",
+    "fsa_append_decode_attn", "fsa_device_memory", "fsa_read_probe",
 )
 
 
@@ -77,6 +77,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             "fsa_describe_step": (i32, [D, C, i32, ctypes.POINTER(i32), i32]),
             "fsa_append_decode_attn": (i32, [D, i32, vp, vp, vp, vp, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                              sz, vp]),
+            "fsa_device_memory": (i32, [ctypes.POINTER(i32), i32]),
+            "fsa_read_probe": (i32, [vp, sz, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -165,6 +167,24 @@ def describe_step(d: Dims, c: LayerCfg, max_seq_len) -> dict:
     r = {k: int(buf[i]) for i, k in enumerate(STEP_INFO[:n])}
     r["plan"] = PLANS[r["plan"]]
     return r
+
+
+MEMORY_INFO = ("memory_clock_khz", "memory_bus_width_bits", "compute_units", "l2_bytes")
+
+
+def device_memory() -> dict:
+    """The current device's memory clock, bus width, CU count and L2 size."""
+    buf = (ctypes.c_int32 * len(MEMORY_INFO))()
+    n = load().fsa_device_memory(buf, len(MEMORY_INFO))
+    if n < 0:
+        raise FsaError(FSA_ERR_HIP, load().fsa_last_error().decode())
+    return {k: int(buf[i]) for i, k in enumerate(MEMORY_INFO[:n])}
+
+
+def read_probe(buf, sink, stream=None):
+    """One plain streaming read of the device tensor buf (the read ceiling)."""
+    _check(load().fsa_read_probe(_p(buf, "buf"), buf.numel() * buf.element_size(), _p(sink, "sink"),
+                                 _stream(stream)))
 
 
 def max_work_items(d: Dims, c: LayerCfg, max_seq_len) -> int:

@@ -466,6 +466,32 @@ int32_t fsa_describe_step(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_s
   return n;
 }
 
+int32_t fsa_device_memory(int32_t* info, int32_t n_info) {
+  if (!info || n_info < 0) {
+    fail(FSA_ERR_INVALID_ARG, "info must be non-null and n_info >= 0");
+    return -1;
+  }
+  int dev = 0;
+  hipDeviceProp_t p;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || hipGetDeviceProperties(&p, dev) != hipSuccess) {
+    fail(FSA_ERR_HIP, "no device properties: %s", hipGetErrorString(e));
+    return -1;
+  }
+  const int32_t v[4] = {p.memoryClockRate, p.memoryBusWidth, p.multiProcessorCount, p.l2CacheSize};
+  const int32_t n = std::min<int32_t>(n_info, 4);
+  for (int32_t i = 0; i < n; ++i) info[i] = v[i];
+  return n;
+}
+
+fsa_status fsa_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  FSA_CHECK(need(buf, "buf"));
+  FSA_CHECK(need(sink, "sink"));
+  if (bytes == 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+    return fail(FSA_ERR_INVALID_ARG, "buf must be 16-byte aligned and bytes a positive multiple of 16 (%zu)", bytes);
+  return hip_status(fsa::launch_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream)), "read probe launch");
+}
+
 size_t fsa_dense_decode_workspace_bytes(const fsa_dims* dims, int32_t max_seq_len) {
   if (check_dims(dims) != FSA_OK || check_len(dims, max_seq_len) != FSA_OK) return 0;
   return dense_ws(dims, max_seq_len).total;

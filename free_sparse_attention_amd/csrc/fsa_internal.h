@@ -107,6 +107,9 @@ __device__ __forceinline__ uint2 ld_nt(const uint2* p) {
 // ---------------------------------------------------------------- device
 
 int device_cu_count();
+// plain streaming read of bytes (a multiple of 16) at buf; sink is written at
+// most once, with a value of no meaning
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 int resident_blocks_per_cu(const void* kernel, int block_threads);
 
 // ---------------------------------------------------------------- launchers

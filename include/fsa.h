@@ -234,6 +234,24 @@ fsa_status fsa_validate_inputs(const fsa_dims* dims, int32_t max_seq_len, const 
                                const int32_t* page_table, const int32_t* seq_lens, int32_t* scratch,
                                void* stream);
 
+/* Measurement helpers (not part of the decode step; the method's pages state
+ * only that long-context decode is bound by reading keys from memory, so the
+ * step's kernels are compared with the device's memory rate).
+ *
+ * fsa_device_memory: properties of the current device, up to n_info of
+ *   info[0] memory clock (kHz), info[1] memory bus width (bits),
+ *   info[2] compute units, info[3] L2 cache bytes (one XCD's).
+ * Returns the number written, or -1 with fsa_last_error() set (no device).
+ *
+ * fsa_read_probe: reads the `bytes` at buf once with coalesced 16-byte
+ * non-temporal loads, on all compute units; its rate is the plain-read
+ * ceiling.  buf: device, 16-byte aligned, bytes a positive multiple of 16.
+ * sink: one device word, written at most once with a value of no meaning.
+ * Asynchronous on stream; FSA_ERR_INVALID_ARG before any launch on bad
+ * arguments. */
+int32_t fsa_device_memory(int32_t* info, int32_t n_info);
+fsa_status fsa_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

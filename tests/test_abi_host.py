@@ -128,3 +128,18 @@ def test_describe_step_rejects_bad_arguments(lib):
     assert lib.fsa_describe_step(ctypes.byref(d), fsa.cfg(16, 64, 4), 1600, None, 8) == -1
     assert lib.fsa_describe_step(ctypes.byref(d), fsa.cfg(16, 64, 4), 1600, buf, 3) == 3
     assert lib.fsa_describe_step(ctypes.byref(d), fsa.cfg(16, 64, 4), 10 ** 9, buf, 8) == -1
+
+
+def test_measurement_helpers_check_their_arguments(lib):
+    sink = ctypes.c_void_p(256)  # never dereferenced: every call below fails before any launch
+    for buf, nbytes in ((None, 1024), (ctypes.c_void_p(4096), 0), (ctypes.c_void_p(4096), 1000),
+                        (ctypes.c_void_p(4104), 1024)):
+        assert lib.fsa_read_probe(buf, nbytes, sink, None) == _lib.FSA_ERR_INVALID_ARG
+    assert lib.fsa_read_probe(ctypes.c_void_p(4096), 1024, None, None) == _lib.FSA_ERR_INVALID_ARG
+    assert lib.fsa_device_memory(None, 4) == -1
+    info = (ctypes.c_int32 * 4)()
+    n = lib.fsa_device_memory(info, 4)
+    if n == -1:  # no device here
+        assert lib.fsa_last_error()
+    else:
+        assert n == 4 and info[0] > 0 and info[1] > 0 and info[2] > 0
