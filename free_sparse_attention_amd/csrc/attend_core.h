@@ -51,23 +51,16 @@ __device__ __forceinline__ void load_q_operand(const uint16_t* q_group, int G, b
   }
 }
 
-// How a wave overlaps its page loads (attend_items):
-enum AttendPipe {
-  kOnePage = 0,    // one page at a time, fewest registers
-  kTwoStage = 1,   // the next page's loads in flight while the current one is computed
-  kStageSecond = 2 // at most two pages: the second goes straight to LDS (the
-                   // wave's own stage) while the first is loaded and computed
-};
-
 // One wave attends its first n items; lane j holds item j's pool page and
-// token range.  n must be wave-uniform (at most 2 with kStageSecond, whose
-// stage is 64 D bytes of LDS, 16-byte aligned, used by this wave alone).
-// head_off/page_stride locate KV head g of a pool page in both caches.
-template <int D, int PIPE>
+// token range.  n must be wave-uniform.  PIPE: two-stage pipeline (the next
+// page's loads in flight while the current page is computed); otherwise one
+// page at a time with fewer registers.  head_off/page_stride locate KV head g
+// of a pool page in both caches.
+template <int D, bool PIPE>
 __device__ __forceinline__ void attend_items(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
                                              size_t head_off, size_t page_stride, const bf16x8_t (&qb)[D / 32],
                                              int my_phys, int my_lo, int my_hi, int n, float scale_log2,
-                                             WaveAttn<D>& st, char* stage = nullptr) {
+                                             WaveAttn<D>& st) {
   constexpr int NKS = D / 32;  // QK k-steps
   constexpr int NDT = D / 16;  // PV d-tiles
   const int lane = threadIdx.x & 63, col = lane & 15, gq = lane >> 4;
@@ -120,35 +113,7 @@ __device__ __forceinline__ void attend_items(const uint16_t* __restrict__ kc, co
     }
   };
 
-  if (PIPE == kStageSecond) {
-    // The page's K block and its V block are 16 D bf16 each, copied in order:
-    // instruction c moves bytes [1024 c, 1024 c + 1024) of a block, 16 per lane.
-    uint4 kA[NKS];
-    uint2 vA[NDT];
-    // the first page's loads go first: while copies into LDS are pending the
-    // compiler waits for every load, so all of them should be in flight then
-    if (n > 0) load(0, kA, vA);
-    if (n > 1) {
-      const size_t blk = (size_t)__builtin_amdgcn_readlane(my_phys, 1) * page_stride + head_off;
-#pragma unroll
-      for (int c = 0; c < NKS; ++c) {
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kc + blk + (size_t)(64 * c + lane) * 8),
-                                         (__attribute__((address_space(3))) void*)(stage + 1024 * c), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vc + blk + (size_t)(64 * c + lane) * 8),
-                                         (__attribute__((address_space(3))) void*)(stage + 32 * D + 1024 * c), 16, 0, 0);
-      }
-    }
-    if (n > 0) compute(0, kA, vA);
-    if (n > 1) {
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the stage is filled
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) kA[ks] = *reinterpret_cast<const uint4*>(stage + 1024 * ks + 16 * lane);
-#pragma unroll
-      for (int t = 0; t < NDT; ++t)
-        vA[t] = *reinterpret_cast<const uint2*>(stage + 32 * D + 2 * ((16 * t + col) * kPage + 4 * gq));
-      compute(1, kA, vA);
-    }
-  } else if (PIPE == kTwoStage) {
+  if (PIPE) {
     // Every trip of the loop issues exactly one page of loads and consumes
     // one, so the number of loads in flight at the loop head is the same on
     // entry and on the back edge and the compiler waits only for the page

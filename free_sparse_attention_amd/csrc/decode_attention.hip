@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256, 3) void decode_attention_kernel(
   bf16x8_t qb[D / 32];
   load_q_operand<D>(q + ((size_t)b * hq + (size_t)g * G) * D, G, qb);
   WaveAttn<D> st;
-  attend_items<D, kTwoStage>(kc, vc, (size_t)g * (kPage * D), (size_t)hkv * (kPage * D), qb, my_phys, my_lo, my_hi, n,
+  attend_items<D, true>(kc, vc, (size_t)g * (kPage * D), (size_t)hkv * (kPage * D), qb, my_phys, my_lo, my_hi, n,
                         scale_log2, st);
   const size_t slot = (size_t)unit * slots_per_unit + slot_base + wg;
   merge_waves<D, kAttnWaves>(S, st, G, direct, out + ((size_t)b * hq + (size_t)g * G) * D, part_o + slot * G * D,

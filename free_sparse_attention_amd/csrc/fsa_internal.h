@@ -91,9 +91,6 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
-// s_waitcnt immediate for vmcnt(0) with the other counters left alone
-constexpr int kWaitVmcnt0 = 0x0F70;
-
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 

@@ -44,6 +44,9 @@ constexpr int kSelMaxPages = kSelThreads * kSelCols;
 constexpr int kSelDigitBits = 11;
 constexpr int kSelBins = 1 << kSelDigitBits;
 
+// s_waitcnt immediate for vmcnt(0) with the other counters left alone
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 struct SelectLds {
   int32_t sphys[kSelMaxPages];  // page-table entries of pages [0, n_max)
   uint32_t hist[2][kSelBins + kWave];  // bins, then one discard slot per lane

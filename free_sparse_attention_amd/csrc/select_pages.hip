@@ -98,7 +98,7 @@ __device__ __forceinline__ void prefix_window_attend(MergeLds<D, kSelWaves>& S, 
   if (my_lo < my_hi && p != p_guess) my_phys = pt[p];
   const int n = __popcll(__ballot(my_lo < my_hi));  // a prefix of the wave's lanes
   WaveAttn<D> st;
-  attend_items<D, kOnePage>(A.kc, A.vc, (size_t)g * (kPage * D), (size_t)A.hkv * (kPage * D), qb, my_phys, my_lo,
+  attend_items<D, false>(A.kc, A.vc, (size_t)g * (kPage * D), (size_t)A.hkv * (kPage * D), qb, my_phys, my_lo,
                          my_hi, n, A.scale_log2, st);
   const size_t slot = (size_t)unit * A.slots_per_unit + wg;
   merge_waves<D, kSelWaves>(S, st, G, false, nullptr, A.part_o + slot * G * D, A.part_ml + 2 * slot * G);
@@ -170,11 +170,8 @@ __device__ __forceinline__ void select_and_attend(SelectLds& SL, MergeLds<D, kSe
   const int n = __popcll(__ballot(my_lo < my_hi));  // a prefix of the wave's lanes
   if (!kCanPrefetch) load_q_operand<D>(A.q + ((size_t)b * A.hq + (size_t)g * G) * D, G, qb);
   WaveAttn<D> st;
-  // at most two selected pages per wave (the plan's per <= 32): the second
-  // is staged in this wave's block of the merge's LDS, which only this wave
-  // writes before the merge's first barrier
-  attend_items<D, kStageSecond>(A.kc, A.vc, (size_t)g * (kPage * D), (size_t)A.hkv * (kPage * D), qb, my_phys,
-                                my_lo, my_hi, n, A.scale_log2, st, reinterpret_cast<char*>(&SM.o[wave][0][0]));
+  attend_items<D, false>(A.kc, A.vc, (size_t)g * (kPage * D), (size_t)A.hkv * (kPage * D), qb, my_phys, my_lo,
+                         my_hi, n, A.scale_log2, st);
   // the prefetch words are used here, after the attention's own loads
   asm volatile("" ::"v"(R.pf[0]), "v"(R.pf[1]), "v"(R.pf[2]), "v"(R.pf[3]));
   const size_t slot = (size_t)unit * A.slots_per_unit + A.pw_wg + r;
