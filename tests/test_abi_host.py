@@ -143,3 +143,10 @@ def test_measurement_helpers_check_their_arguments(lib):
         assert lib.fsa_last_error()
     else:
         assert n == 4 and info[0] > 0 and info[1] > 0 and info[2] > 0
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without the built library the binding raises; nothing falls back to a CPU path."""
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load("/nonexistent/libfsa.so")
