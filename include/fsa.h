@@ -193,7 +193,8 @@ int32_t fsa_describe_step(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_s
 
 /* fsa_append_kv followed by fsa_sparse_decode_attn on the same stream, as one
  * call: the decode step of a model that has just produced the new tokens'
- * K/V.  Results (caches, metadata, seq_lens_out, out, sel_pages) equal those
+ * K/V (the per-layer decode step of the paper's Abstract and the digest
+ * page's "The Move", over a cache that grows by n_new tokens first).  Results (caches, metadata, seq_lens_out, out, sel_pages) equal those
  * of the two calls bit for bit.  When no page the append writes can be a
  * candidate of the step (window_tokens >= n_new + 15, and more candidates
  * than the budget) the append runs inside the scoring launch, one launch
