@@ -553,7 +553,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="ctx64k")
+    ap.add_argument("--workload", default="ctx64k", help="tiny, ctx64k or ctx256k")
     ap.add_argument("--no-also", action="store_true", help="skip the 256k measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
