@@ -310,13 +310,21 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
     return res
 
 
-SWEEP_LENS = (2048, 4096, 8192, 16384, 32768, 65536, 131072, 262144)
+SWEEP_LENS = (2048, 4096, 8192, 16384, 32768, 65536, 131072, 262144, 524288)
 
 
 def crossover_sweep(steps, warmup):
     """Sparse and dense step times at the 64k workload's shapes (batch 4, Hq 16 / Hkv 4,
-    D 128, prefix 128, window 1024, budget 128 pages) for context lengths 2k..256k."""
+    D 128, prefix 128, window 1024, budget 128 pages) for context lengths 2k..512k."""
     import synth
+    import torch
+    # bring the clocks up before the first (shortest, latency-bound) point
+    a = torch.randn(4096, 4096, device="cuda")
+    t_end = time.time() + 0.5
+    while time.time() < t_end:
+        a = torch.tanh(a @ a)
+        torch.cuda.synchronize()
+    del a
     rows = []
     for L in SWEEP_LENS:
         wl = synth.make_workload("ctx64k", seq_lens=(L,) * 4)
@@ -558,7 +566,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--sweep", action="store_true",
-                    help="instead: sparse vs dense step time for context lengths 2k..256k")
+                    help="instead: sparse vs dense step time for context lengths 2k..512k")
     ap.add_argument("--ragged", action="store_true",
                     help="instead: the 16-sequence serving batch, one-token append + sparse decode per step")
     ap.add_argument("--layers12", action="store_true",
