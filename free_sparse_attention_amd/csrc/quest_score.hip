@@ -29,7 +29,6 @@
 namespace fsa {
 namespace {
 
-constexpr int kScoreWaves = 4;  // waves per workgroup
 
 __device__ __forceinline__ uint32_t keep_sign(uint32_t w, bool negative) {
   // per 16-bit half: keep it when its sign matches `negative`, else zero it
@@ -53,8 +52,8 @@ __device__ __forceinline__ uint32_t keep_sign(uint32_t w, bool negative) {
 // candidate (window >= n_new + 15), so the two roles write and read disjoint
 // data; the scores of the touched pages' tiles that are not candidates are
 // computed from metadata being rewritten, but never stored.
-template <int D>
-__global__ __launch_bounds__(kScoreWaves * 64) void quest_score_kernel(
+template <int D, int W>  // W: waves per workgroup
+__global__ __launch_bounds__(W * 64) void quest_score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ meta,
     const int32_t* __restrict__ seq_lens, float* __restrict__ scores, int hq, int hkv,
     int max_pages, int prefix, int window, int tiles_per_wave, int wg_per_unit, int max_seq_len,
@@ -62,7 +61,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void quest_score_kernel(
   constexpr int NSTEP = 2 * D / 32;  // k-steps over the 2D metadata values
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if ((int)blockIdx.x < append_blocks) {
-    const int w = (int)blockIdx.x * kScoreWaves + wave;
+    const int w = (int)blockIdx.x * W + wave;
     if (w < append_tasks) append_task<D>(ap, w, lane);
     return;
   }
@@ -75,8 +74,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void quest_score_kernel(
   // tile is known before the length arrives and is loaded together with it.
   const int c_lo_h = min(prefix, max_seq_len) / kPage;
   const int c_hi_h = (max(0, max_seq_len - window) + kPage - 1) / kPage;
-  const int n_waves = kScoreWaves * wg_per_unit;
-  const int t_first = c_lo_h / kMetaTile + wg * kScoreWaves + wave;  // then every n_waves-th tile
+  const int n_waves = W * wg_per_unit;
+  const int t_first = c_lo_h / kMetaTile + wg * W + wave;  // then every n_waves-th tile
   const int t_end_h = max(1, (c_hi_h + kMetaTile - 1) / kMetaTile);
 
   // A operand: row `col` = query head col of the group (zero beyond G).
@@ -161,22 +160,28 @@ hipError_t launch_quest_scores(const uint16_t* q, const uint16_t* meta, const in
   const int units = batch * hkv;
   const int max_cand = (max_seq_len + kPage - 1) / kPage;
   const int tiles_per_unit = (max_cand + kMetaTile - 1) / kMetaTile + 1;  // a range may straddle one more
-  const void* kern = d == 128 ? reinterpret_cast<const void*>(&quest_score_kernel<128>)
-                              : reinterpret_cast<const void*>(&quest_score_kernel<64>);
-  static std::atomic<int> resident[2];  // per head dim, zero until first queried
-  int res = resident[d == 128].load(std::memory_order_relaxed);
+  // 8-wave workgroups for batches of many units (the 16-sequence serving
+  // batch: 128 units, step 171 -> 169 us), 4-wave ones otherwise (64k and
+  // 256k: 4 waves 0.1 and 0.9 us faster)
+  const int W = units >= 64 ? 8 : 4;
+  const void* kern = d == 128 ? (W == 8 ? reinterpret_cast<const void*>(&quest_score_kernel<128, 8>)
+                                        : reinterpret_cast<const void*>(&quest_score_kernel<128, 4>))
+                              : (W == 8 ? reinterpret_cast<const void*>(&quest_score_kernel<64, 8>)
+                                        : reinterpret_cast<const void*>(&quest_score_kernel<64, 4>));
+  static std::atomic<int> resident[2][2];  // per head dim and workgroup size, zero until first queried
+  int res = resident[d == 128][W == 8].load(std::memory_order_relaxed);
   if (res == 0) {
-    res = resident_blocks_per_cu(kern, kScoreWaves * 64);
-    resident[d == 128].store(res, std::memory_order_relaxed);
+    res = resident_blocks_per_cu(kern, W * 64);
+    resident[d == 128][W == 8].store(res, std::memory_order_relaxed);
   }
   // four resident rounds of workgroups shared out over the units: workgroups
   // whose tiles lie beyond their sequence's length exit at once and the
   // dispatcher gives their slots to the next ones, which evens out batches of
   // unequal lengths (16 sequences of 18k-261k tokens: step 165.9 -> 158.9 us)
   const int round = 4 * res * device_cu_count();
-  const int wg_per_unit_max = (tiles_per_unit + kScoreWaves - 1) / kScoreWaves;
+  const int wg_per_unit_max = (tiles_per_unit + W - 1) / W;
   const int wg_per_unit = std::max(1, std::min(wg_per_unit_max, round / std::max(1, units)));
-  const int tpw = (tiles_per_unit + kScoreWaves * wg_per_unit - 1) / (kScoreWaves * wg_per_unit);
+  const int tpw = (tiles_per_unit + W * wg_per_unit - 1) / (W * wg_per_unit);
   AppendArgs ap{};
   int append_tasks = 0, len_add = 0;
   if (append) {
@@ -184,16 +189,18 @@ hipError_t launch_quest_scores(const uint16_t* q, const uint16_t* meta, const in
     append_tasks = units * ap.touch;
     len_add = ap.n_new;
   }
-  const int append_blocks = (append_tasks + kScoreWaves - 1) / kScoreWaves;
+  const int append_blocks = (append_tasks + W - 1) / W;
   const dim3 grid((unsigned)((long)append_blocks + (long)units * wg_per_unit));
-  if (d == 128)
-    hipLaunchKernelGGL(quest_score_kernel<128>, grid, dim3(kScoreWaves * 64), 0, stream, q, meta, seq_lens,
-                       scores, hq, hkv, max_pages, prefix, window, tpw, wg_per_unit, max_seq_len, ap,
-                       append_blocks, append_tasks, len_add);
-  else
-    hipLaunchKernelGGL(quest_score_kernel<64>, grid, dim3(kScoreWaves * 64), 0, stream, q, meta, seq_lens,
-                       scores, hq, hkv, max_pages, prefix, window, tpw, wg_per_unit, max_seq_len, ap,
-                       append_blocks, append_tasks, len_add);
+#define FSA_SCORE(DD, WW)                                                                                       \
+  hipLaunchKernelGGL((quest_score_kernel<DD, WW>), grid, dim3(WW * 64), 0, stream, q, meta, seq_lens, scores, hq, \
+                     hkv, max_pages, prefix, window, tpw, wg_per_unit, max_seq_len, ap, append_blocks, append_tasks,  \
+                     len_add)
+  if (d == 128) {
+    if (W == 8) FSA_SCORE(128, 8); else FSA_SCORE(128, 4);
+  } else {
+    if (W == 8) FSA_SCORE(64, 8); else FSA_SCORE(64, 4);
+  }
+#undef FSA_SCORE
   return hipGetLastError();
 }
 

@@ -325,17 +325,22 @@ def test_append_matches_rebuild_and_oracle():
     run_and_check(wl, dw=dw)
 
 
-@pytest.mark.parametrize("cfg,chunks", [((128, 1024, 16), [1, 1, 37, 1, 16, 1]),  # append inside the scoring launch
-                                        ((32, 10, 8), [1, 5, 1, 7]),  # window < n_new + 15: append launched first
-                                        ((16, 4096, 64), [3, 1])])  # every candidate fits the budget: dense path
-def test_append_decode_equals_append_then_decode(cfg, chunks):
+@pytest.mark.parametrize("cfg,chunks,many", [
+    ((128, 1024, 16), [1, 1, 37, 1, 16, 1], False),  # append inside the scoring launch
+    ((128, 1024, 16), [1, 3, 1], True),  # the same with 64 units (8-wave scoring workgroups)
+    ((32, 10, 8), [1, 5, 1, 7], False),  # window < n_new + 15: append launched first
+    ((16, 4096, 64), [3, 1], False)])  # every candidate fits the budget: dense path
+def test_append_decode_equals_append_then_decode(cfg, chunks, many):
     """fsa_append_decode_attn gives bit for bit the caches, metadata, lengths,
     output and selection of fsa_append_kv followed by fsa_sparse_decode_attn,
     step after step, with the append fused into the scoring launch or not."""
     import free_sparse_attention_amd as fsa
-    wl = synth.workloads.build(name="appdec", seed=21, batch=3, hq=8, hkv=2, d=128, seq_lens=(3000, 1999, 4095),
-                               prefix=cfg[0], window=cfg[1], budget=cfg[2], k_sigma=0.5, permuted=True,
-                               extra_tokens=200)
+    if many:
+        shape = dict(batch=16, hq=16, hkv=4, seq_lens=tuple(3000 + 517 * i for i in range(16)))
+    else:
+        shape = dict(batch=3, hq=8, hkv=2, seq_lens=(3000, 1999, 4095))
+    wl = synth.workloads.build(name="appdec", seed=21, d=128, prefix=cfg[0], window=cfg[1], budget=cfg[2],
+                               k_sigma=0.5, permuted=True, extra_tokens=200, **shape)
     a, b = DeviceWorkload(wl), DeviceWorkload(wl)
     c = fsa.cfg(*cfg)
     msl = int(wl.seq_lens.max()) + sum(chunks)
