@@ -37,8 +37,8 @@ __device__ __forceinline__ uint32_t keep_sign(uint32_t w, bool negative) {
   return negative ? (w & neg_mask) : (w & ~neg_mask);
 }
 
-// Each wave scores every W-th 16-page tile of one (sequence, KV head) unit,
-// W being the unit's wave count, so at any moment the unit's waves together
+// Each wave scores every n-th 16-page tile of one (sequence, KV head) unit,
+// n being the unit's wave count, so at any moment the unit's waves together
 // read one contiguous stretch of metadata; the grid is sized to four resident
 // rounds of waves.  Metadata is loaded one tile ahead of the MFMA chain, with
 // the non-temporal hint: it is read once per step and should not displace
