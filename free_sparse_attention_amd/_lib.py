@@ -73,7 +73,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             "fsa_sparse_decode_attn": (i32, [D, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "fsa_dense_decode_workspace_bytes": (sz, [D, i32]),
             "fsa_dense_decode_attn": (i32, [D, f32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
-            "fsa_validate_inputs": (i32, [D, i32, vp, vp, vp, vp, vp]),
+            "fsa_validate_inputs": (i32, [D, i32, i32, vp, vp, vp, vp, vp]),
             "fsa_describe_step": (i32, [D, C, i32, ctypes.POINTER(i32), i32]),
             "fsa_append_decode_attn": (i32, [D, i32, vp, vp, vp, vp, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                              sz, vp]),
@@ -154,7 +154,8 @@ def quest_scores(d: Dims, c: LayerCfg, max_seq_len, q, meta, seq_lens, scores, s
                                    _i32(seq_lens, "seq_lens"), _p(scores, "scores", 4), _stream(stream)))
 
 
-STEP_INFO = ("plan", "replicas", "per_replica", "xcd_grouped", "prefetch", "pw_workgroups", "slots", "select_cols")
+STEP_INFO = ("plan", "replicas", "per_replica", "xcd_grouped", "prefetch", "pw_workgroups", "slots", "select_cols",
+             "pw_items_per_wave")
 PLANS = {0: "dense", 1: "wide", 2: "narrow"}
 
 
@@ -244,10 +245,11 @@ def dense_decode_attn(d: Dims, sm_scale, max_seq_len, q, k_cache, v_cache, page_
         _stream(stream)))
 
 
-def validate_inputs(d: Dims, max_seq_len, q, page_table, seq_lens, scratch=None, stream=None) -> None:
-    """Debug check of device inputs (synchronises); raises FsaError naming a violation."""
+def validate_inputs(d: Dims, max_seq_len, q, page_table, seq_lens, scratch=None, stream=None, n_new=0) -> None:
+    """Debug check of device inputs (synchronises); raises FsaError naming a violation.
+    With n_new > 0 the lengths are checked as they will be after appending n_new tokens."""
     if scratch is None:
         scratch = torch.empty(4, dtype=torch.int32, device=page_table.device)
     _check(load().fsa_validate_inputs(
-        ctypes.byref(d), int(max_seq_len), _p(q, "q", 2) if q is not None else None,
+        ctypes.byref(d), int(n_new), int(max_seq_len), _p(q, "q", 2) if q is not None else None,
         _i32(page_table, "page_table"), _i32(seq_lens, "seq_lens"), _i32(scratch, "scratch"), _stream(stream)))

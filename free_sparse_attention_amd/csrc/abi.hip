@@ -1,4 +1,4 @@
-// C-ABI entry points declared in include/fsa.h: host-side argument checks,
+// C-ABI entry points declared in include/fsa.h and include/fsa_measure.h: host-side argument checks,
 // workspace layout and launch sequencing on the caller's stream.
 #include <stdarg.h>
 #include <stdio.h>
@@ -7,6 +7,7 @@
 #include <string>
 
 #include "../../include/fsa.h"
+#include "../../include/fsa_measure.h"
 #include "append_core.h"
 
 namespace {
@@ -310,9 +311,10 @@ size_t fsa_sparse_decode_workspace_bytes(const fsa_dims* dims, fsa_layer_cfg cfg
 
 namespace {
 
-fsa_status check_step(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_scale, int32_t max_seq_len, const void* q,
-                      const void* k_cache, const void* v_cache, const void* meta, const int32_t* page_table,
-                      const int32_t* seq_lens, void* out, void* workspace, size_t workspace_bytes) {
+// Every host check of a decode step but the workspace's.
+fsa_status check_step_args(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_scale, int32_t max_seq_len,
+                           const void* q, const void* k_cache, const void* v_cache, const void* meta,
+                           const int32_t* page_table, const int32_t* seq_lens, void* out) {
   FSA_CHECK(check_dims(dims));
   FSA_CHECK(check_cfg(cfg));
   FSA_CHECK(check_len(dims, max_seq_len));
@@ -324,6 +326,13 @@ fsa_status check_step(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_scale, i
   FSA_CHECK(need(seq_lens, "seq_lens"));
   FSA_CHECK(need(out, "out"));
   if (!(sm_scale > 0.f)) return fail(FSA_ERR_INVALID_ARG, "sm_scale must be > 0");
+  return FSA_OK;
+}
+
+fsa_status check_step(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_scale, int32_t max_seq_len, const void* q,
+                      const void* k_cache, const void* v_cache, const void* meta, const int32_t* page_table,
+                      const int32_t* seq_lens, void* out, void* workspace, size_t workspace_bytes) {
+  FSA_CHECK(check_step_args(dims, cfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table, seq_lens, out));
   const size_t total = sparse_ws(dims, cfg, max_seq_len).total;
   if (!workspace || workspace_bytes < total)
     return fail(FSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, total);
@@ -453,15 +462,16 @@ int32_t fsa_describe_step(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_s
     return -1;
   }
   const SparseWs w = sparse_ws(dims, cfg, max_seq_len);
-  const int32_t v[8] = {w.all_taken ? 0 : (w.step.sel_rep > 0 ? 1 : 2),
+  const int32_t v[9] = {w.all_taken ? 0 : (w.step.sel_rep > 0 ? 1 : 2),
                         w.step.sel_rep,
                         w.step.sel_rep > 0 ? w.step.per : 0,
                         w.step.xcd_grouped,
                         w.step.prefetch,
                         w.all_taken ? 0 : w.step.pw.wg_per_unit,
                         w.slots,
-                        fsa::select_columns(max_seq_len)};
-  const int32_t n = std::min<int32_t>(n_info, 8);
+                        fsa::select_columns(max_seq_len),
+                        w.all_taken ? 0 : w.step.pw.ipw};
+  const int32_t n = std::min<int32_t>(n_info, 9);
   for (int32_t i = 0; i < n; ++i) info[i] = v[i];
   return n;
 }
@@ -520,18 +530,20 @@ fsa_status fsa_dense_decode_attn(const fsa_dims* dims, float sm_scale, int32_t m
                     "dense decode attention launch");
 }
 
-fsa_status fsa_validate_inputs(const fsa_dims* dims, int32_t max_seq_len, const void* q,
+fsa_status fsa_validate_inputs(const fsa_dims* dims, int32_t n_new, int32_t max_seq_len, const void* q,
                                const int32_t* page_table, const int32_t* seq_lens, int32_t* scratch,
                                void* stream) {
   FSA_CHECK(check_dims(dims));
   FSA_CHECK(check_len(dims, max_seq_len));
+  if (n_new < 0) return fail(FSA_ERR_INVALID_ARG, "n_new must be >= 0");
   FSA_CHECK(need(page_table, "page_table"));
   FSA_CHECK(need(seq_lens, "seq_lens"));
   FSA_CHECK(need(scratch, "scratch"));
   hipStream_t st = static_cast<hipStream_t>(stream);
   FSA_CHECK(hip_status(fsa::launch_validate(static_cast<const uint16_t*>(q), page_table, seq_lens, scratch,
                                             dims->batch, q ? dims->num_q_heads : 0, dims->head_dim,
-                                            dims->max_pages_per_seq, dims->num_pool_pages, max_seq_len, st),
+                                            dims->max_pages_per_seq, dims->num_pool_pages, max_seq_len, n_new,
+                                            st),
                        "validate launch"));
   int32_t h[4];
   FSA_CHECK(hip_status(hipMemcpyAsync(h, scratch, sizeof(h), hipMemcpyDeviceToHost, st), "validate copy"));
@@ -539,8 +551,16 @@ fsa_status fsa_validate_inputs(const fsa_dims* dims, int32_t max_seq_len, const 
   if (h[0] == 0) return FSA_OK;
   switch (h[1]) {
     case 1:
+      if (n_new > 0)
+        return fail(FSA_ERR_INVALID_ARG, "%d invalid inputs; e.g. seq_lens[%d] = %d: with %d new tokens outside [0, %d]",
+                    h[0], h[2], h[3], n_new, max_seq_len - n_new);
       return fail(FSA_ERR_INVALID_ARG, "%d invalid inputs; e.g. seq_lens[%d] = %d outside [1, %d]", h[0], h[2], h[3],
                   max_seq_len);
+    case 4:
+      return fail(FSA_ERR_INVALID_ARG,
+                  "%d invalid inputs; e.g. sequence %d overflows its page table: seq_lens[%d] = %d plus %d new tokens "
+                  "exceeds %d pages of 16 tokens",
+                  h[0], h[2], h[2], h[3], n_new, dims->max_pages_per_seq);
     case 2:
       return fail(FSA_ERR_INVALID_ARG, "%d invalid inputs; e.g. page_table[%d][%d] outside [0, %d)", h[0], h[2], h[3],
                   dims->num_pool_pages);

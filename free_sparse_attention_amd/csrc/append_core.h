@@ -99,9 +99,13 @@ __device__ __forceinline__ void append_task(const AppendArgs& A, int w, int lane
   const int L0 = A.seq_lens[b];
   const int slot = lane % kPage;
   const int n_new = A.n_new, max_pages = A.max_pages, hkv = A.hkv;
-  if (A.seq_lens_out != nullptr && g == 0 && j == 0 && lane == 0) A.seq_lens_out[b] = L0 + n_new;
+  // Positions past the page table are dropped, and the length counts only
+  // the tokens written (fsa_validate_inputs reports such an overflow).
+  const int cap = max_pages * kPage;
+  if (A.seq_lens_out != nullptr && g == 0 && j == 0 && lane == 0)
+    A.seq_lens_out[b] = L0 + n_new <= cap ? L0 + n_new : max(L0, cap);
   const int p = L0 / kPage + j;
-  if (p >= max_pages) return;  // positions past the page table are dropped
+  if (p >= max_pages) return;
   const int t_lo = max(L0, p * kPage), t_hi = min(L0 + n_new, p * kPage + kPage);
   if (t_lo >= t_hi) return;
   const int s0 = t_lo - p * kPage, s1 = t_hi - p * kPage;

@@ -153,7 +153,7 @@ struct AttnPlan {
 // Debug validation of device inputs into scratch (int32[4]); see fsa_validate_inputs.
 hipError_t launch_validate(const uint16_t* q, const int32_t* page_table, const int32_t* seq_lens,
                            int32_t* scratch, int batch, int hq, int d, int max_pages, int pool,
-                           int max_seq_len, hipStream_t stream);
+                           int max_seq_len, int n_new, hipStream_t stream);
 
 // One decode step's selection launch: the top-k selection of every (sequence,
 // KV head) with the attention over the selected pages, plus the attention over

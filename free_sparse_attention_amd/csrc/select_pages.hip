@@ -249,7 +249,10 @@ PwPlan plan_prefix_window(int units, int pw_cus, int prefix, int window, int max
   const int pre = std::min((prefix + kPage - 1) / kPage, n_max);
   const int win = std::min((window + kPage - 1) / kPage + 1, n_max);
   PwPlan p;
-  p.max_items = std::min(pre + win, n_max);
+  // Not clamped to n_max: when the prefix ends and the window starts on the
+  // same page, that page is one prefix item and one window item, so a
+  // sequence can need n_pages + 1 items.
+  p.max_items = pre + win;
   if (p.max_items == 0) {
     p.ipw = 1;
     p.wg_per_unit = 0;

@@ -27,6 +27,18 @@
  *     FSA_ERR_HIP.  Device-resident data (page tables, lengths) is trusted.
  *   - bf16 tensors are raw IEEE bfloat16 bit patterns.
  *
+ * Why the cache layout is not the common token-major [pool][Hkv][S][D]
+ *   The decode step reads each selected page once, straight into the matrix
+ *   cores.  With K stored chunk-major ([D/8][S][8]) one 64-lane load of a
+ *   page's K is one contiguous 1 KiB row in exactly the operand order of a
+ *   16x16x32 bf16 MFMA step, and with V stored channel-major ([D][S]) the P.V
+ *   operand of a lane is 8 contiguous bytes.  A cache kept by a model in the
+ *   token-major layout is adopted once with fsa_import_kv_plain (and its
+ *   metadata built with fsa_build_page_meta); fsa_append_kv then keeps both
+ *   current.  Metadata is per (sequence, logical page) rather than per pool
+ *   page: it is derived state of the sequence, so the scoring pass streams it
+ *   without a page-table lookup.
+ *
  * Device layouts (row-major, no padding)
  *   q, out      bf16  [B][Hq][D]            query head h reads KV head h / (Hq/Hkv)
  *   k_cache     bf16  [pool][Hkv][D/8][S][8] K of token slot j, channel c of a page
@@ -74,8 +86,8 @@ typedef struct {
   int32_t num_kv_heads;      /* Hkv */
   int32_t head_dim;          /* D */
   int32_t page_size;         /* S, tokens per page */
-  int32_t max_pages_per_seq; /* columns of page_table */
-  int32_t num_pool_pages;    /* pages in k_cache, v_cache and meta */
+  int32_t max_pages_per_seq; /* columns of page_table; also sizes meta (kept per sequence) */
+  int32_t num_pool_pages;    /* pages in k_cache and v_cache */
 } fsa_dims;
 
 /* Per-layer configuration (paper, Abstract: window and budget are chosen per
@@ -100,30 +112,46 @@ fsa_status fsa_import_kv_plain(const fsa_dims* dims, const void* k_plain, const 
                                void* k_cache, void* v_cache, void* stream);
 
 /* Append n_new >= 1 tokens to every sequence and keep the page metadata
- * current (Quest's per-page key min/max).  Token i of sequence b goes to
- * position seq_lens[b] + i, i.e. page page_table[b][pos / S], slot pos % S;
- * those page-table entries must already be mapped.
+ * current: the per-page elementwise key minimum and maximum that Quest's
+ * bound needs (analysis page "Methodology" and digest page "The Move" name
+ * Quest as the selection rule; the decode step of the paper's Abstract runs
+ * after each new token).  Token i of sequence b goes to position
+ * seq_lens[b] + i, i.e. page page_table[b][pos / S], slot pos % S; those
+ * page-table entries must already be mapped.
  *   k_new, v_new  bf16 [B][n_new][Hkv][D] (device)
  *   seq_lens      int32 [B] (device), lengths before the append
- *   seq_lens_out  int32 [B] (device) or NULL; receives seq_lens[b] + n_new
- *                 (must not alias seq_lens)
+ *   seq_lens_out  int32 [B] (device) or NULL; receives the lengths after the
+ *                 append, seq_lens[b] + n_new (must not alias seq_lens)
  * A page whose slot 0 is written by this call gets fresh metadata from the
  * new tokens only; otherwise the new tokens' min/max are merged into the
- * existing entry.  The result equals fsa_build_page_meta bit for bit. */
+ * existing entry.  The result equals fsa_build_page_meta bit for bit.
+ * Capacity: positions at or past max_pages_per_seq * S have no page and are
+ * not written; seq_lens_out then counts only the tokens written
+ * (min(seq_lens[b] + n_new, max_pages_per_seq * S)).  Lengths live on the
+ * device, so the host cannot see this; fsa_validate_inputs with n_new
+ * reports it before the append. */
 fsa_status fsa_append_kv(const fsa_dims* dims, int32_t n_new, const void* k_new, const void* v_new,
                          const int32_t* page_table, const int32_t* seq_lens, int32_t* seq_lens_out,
                          void* k_cache, void* v_cache, void* meta, void* stream);
 
 /* Recompute the metadata of every page in use (logical pages
  * [0, ceil(seq_lens[b] / S)) of every sequence) from k_cache, over each
- * page's valid slots only.  Entries of pages not in use are not written. */
+ * page's valid slots only: Quest's per-page elementwise key minimum and
+ * maximum (the selection rule of the analysis page's "Methodology" and the
+ * digest's "The Move"), for a cache filled by prefill or adopted with
+ * fsa_import_kv_plain.  Entries of pages not in use are not written.
+ *   k_cache   bf16, layout above (device)
+ *   meta      bf16, layout above (device), fsa_meta_bytes() bytes
+ * Exact (min and max involve no rounding); asynchronous on stream. */
 fsa_status fsa_build_page_meta(const fsa_dims* dims, const void* k_cache, const int32_t* page_table,
                                const int32_t* seq_lens, void* meta, void* stream);
 
 /* Bytes of the page-metadata buffer for these dims (0 on invalid dims). */
 size_t fsa_meta_bytes(const fsa_dims* dims);
 
-/* Quest scores of the candidate pages.  For every (b, KV head g) and every
+/* Quest scores of the candidate pages: the query-aware relevance that the
+ * paged top-k ranks by (analysis page "Methodology", digest page "The
+ * Move"; the bound is Quest's).  For every (b, KV head g) and every
  * candidate logical page p:
  *     scores[b][g][p] = max over query heads h of group g of
  *                       sum_i max(q[b][h][i] * m[p][i], q[b][h][i] * M[p][i])
@@ -138,7 +166,9 @@ fsa_status fsa_quest_scores(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max
 /* Number of work items per (b, KV head) that fsa_select_pages can emit. */
 int32_t fsa_max_work_items(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len);
 
-/* Top-k selection and merge with the prefix and the window.
+/* Top-k selection and merge with the prefix and the window: the fixed
+ * budget of most relevant pages next to the pinned prefix and the sliding
+ * window (paper, Abstract; a paged top-k per the digest's "The Move").
  * For every (b, g): the k = min(budget, C) candidate pages with the largest
  * scores; equal scores go to the lower logical page id; -0 equals +0.
  *   sel_pages  int32 [B][Hkv][budget_pages] (device) or NULL: selected logical
@@ -159,9 +189,14 @@ fsa_status fsa_select_pages(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max
 /* Workspace (device bytes) that fsa_sparse_decode_attn needs. */
 size_t fsa_sparse_decode_workspace_bytes(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len);
 
-/* The whole decode step: scores, selection and merge, then split-K flash
- * decoding over the attended tokens (fp32 logits, online softmax and fp32
- * accumulation) and the cross-split combine.
+/* The whole decode step of one full-attention layer (paper, Abstract: the
+ * query attends to the pinned prefix, the sliding window and a fixed budget
+ * of the most relevant tokens; analysis page "Methodology" and digest page
+ * "The Move": chosen by a Quest-style paged top-k; digest page "Why It
+ * Matters": the cache stays full size, so every page can be chosen):
+ * scores, selection and merge, then split-K flash decoding over the
+ * attended tokens (fp32 logits, online softmax and fp32 accumulation) and
+ * the cross-split combine.
  *   out        bf16 [B][Hq][D] (device): softmax(sm_scale * q.K) V over the
  *              attended set, rounded to nearest-even bf16
  *   sel_pages  as in fsa_select_pages, or NULL
@@ -187,6 +222,8 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
  *   info[5]  prefix/window workgroups per unit
  *   info[6]  partial slots per unit (merged by the combine)
  *   info[7]  pages per selection thread (a power of two)
+ *   info[8]  prefix/window items each wave of a prefix/window workgroup
+ *            attends (16 waves per workgroup)
  * Returns the number of entries written, or -1 with fsa_last_error() set. */
 int32_t fsa_describe_step(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len, int32_t* info,
                           int32_t n_info);
@@ -215,43 +252,35 @@ fsa_status fsa_append_decode_attn(const fsa_dims* dims, int32_t n_new, const voi
 size_t fsa_dense_decode_workspace_bytes(const fsa_dims* dims, int32_t max_seq_len);
 
 /* Plain decode attention over all tokens [0, seq_lens[b]) with the same
- * split-K kernels: the baseline that the sparse step is measured against.
- * The workspace needs no initial contents. */
+ * split-K kernels: the full attention whose every-step read of all keys the
+ * method avoids (digest page, opening and "Why It Matters"), kept as the
+ * baseline that the sparse step is measured against, and the result the
+ * sparse step must equal when its budget covers every page.
+ *   q, out  bf16 [B][Hq][D] (device); caches and page table as above
+ * The workspace needs no initial contents; FSA_ERR_WORKSPACE if it is
+ * smaller than fsa_dense_decode_workspace_bytes(). */
 fsa_status fsa_dense_decode_attn(const fsa_dims* dims, float sm_scale, int32_t max_seq_len,
                                  const void* q, const void* k_cache, const void* v_cache,
                                  const int32_t* page_table, const int32_t* seq_lens, void* out,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
-/* Debug check of the device-resident inputs of a decode step; unlike every
- * other call it synchronises `stream` and is not graph-capturable.  Checks
- * that every seq_lens[b] lies in [1, max_seq_len], that page_table[b][p] lies
- * in [0, num_pool_pages) for every page p < ceil(seq_lens[b] / S) in use, and
- * that every value of q (bf16 [B][Hq][D], device; may be NULL to skip) is
- * finite.  The other entry points trust these values.
+/* Debug check of the device-resident inputs of a decode step or of an
+ * append; unlike every other call it synchronises `stream` and is not
+ * graph-capturable.  With n_new = 0 (a decode step) it checks that every
+ * seq_lens[b] lies in [1, max_seq_len].  With n_new > 0 (an append of n_new
+ * tokens, before it runs) it checks that seq_lens[b] >= 0, that
+ * seq_lens[b] + n_new fits the page table (max_pages_per_seq * S tokens;
+ * a sequence that does not is named as overflowing it) and that it is at
+ * most max_seq_len.  Either way page_table[b][p] must lie in
+ * [0, num_pool_pages) for every page p < ceil((seq_lens[b] + n_new) / S),
+ * and every value of q (bf16 [B][Hq][D], device; may be NULL to skip) must
+ * be finite.  The other entry points trust these values.
  *   scratch  int32[4] (device), caller-owned, no initial contents needed
  * Returns FSA_OK, or FSA_ERR_INVALID_ARG with fsa_last_error() naming the
  * number of violations and one of them. */
-fsa_status fsa_validate_inputs(const fsa_dims* dims, int32_t max_seq_len, const void* q,
+fsa_status fsa_validate_inputs(const fsa_dims* dims, int32_t n_new, int32_t max_seq_len, const void* q,
                                const int32_t* page_table, const int32_t* seq_lens, int32_t* scratch,
                                void* stream);
-
-/* Measurement helpers (not part of the decode step; the method's pages state
- * only that long-context decode is bound by reading keys from memory, so the
- * step's kernels are compared with the device's memory rate).
- *
- * fsa_device_memory: properties of the current device, up to n_info of
- *   info[0] memory clock (kHz), info[1] memory bus width (bits),
- *   info[2] compute units, info[3] L2 cache bytes (one XCD's).
- * Returns the number written, or -1 with fsa_last_error() set (no device).
- *
- * fsa_read_probe: reads the `bytes` at buf once with coalesced 16-byte
- * non-temporal loads, on all compute units; its rate is the plain-read
- * ceiling.  buf: device, 16-byte aligned, bytes a positive multiple of 16.
- * sink: one device word, written at most once with a value of no meaning.
- * Asynchronous on stream; FSA_ERR_INVALID_ARG before any launch on bad
- * arguments. */
-int32_t fsa_device_memory(int32_t* info, int32_t n_info);
-fsa_status fsa_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

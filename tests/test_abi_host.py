@@ -1,6 +1,7 @@
 """The C-ABI library loads, exports every entry point of include/fsa.h, and
 rejects bad host arguments before touching a GPU (no device needed)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -10,13 +11,15 @@ import free_sparse_attention_amd as fsa
 from free_sparse_attention_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "fsa.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fsa_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(fsa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -92,9 +95,11 @@ def test_bad_cfg_len_and_pointers(lib):
     assert lib.fsa_append_decode_attn(ctypes.byref(d), 1, p, p, p, ctypes.c_void_p(32), c, 0.125, 4096, p, p, p, p,
                                       p, p, None, p, need - 1, None) == _lib.FSA_ERR_WORKSPACE
     # the validator checks its host arguments before any launch
-    assert lib.fsa_validate_inputs(ctypes.byref(d), 4096, p, p, p, None, None) == _lib.FSA_ERR_INVALID_ARG
+    assert lib.fsa_validate_inputs(ctypes.byref(d), 0, 4096, p, p, p, None, None) == _lib.FSA_ERR_INVALID_ARG
     assert b"scratch" in lib.fsa_last_error()
-    assert lib.fsa_validate_inputs(ctypes.byref(d), 0, p, p, p, p, None) == _lib.FSA_ERR_INVALID_ARG
+    assert lib.fsa_validate_inputs(ctypes.byref(d), 0, 0, p, p, p, p, None) == _lib.FSA_ERR_INVALID_ARG
+    assert lib.fsa_validate_inputs(ctypes.byref(d), -1, 4096, p, p, p, p, None) == _lib.FSA_ERR_INVALID_ARG
+    assert b"n_new" in lib.fsa_last_error()
 
 
 def _plan(B, hq, hkv, D, L, P, W, budget):
@@ -150,3 +155,37 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load("/nonexistent/libfsa.so")
+
+
+def _pw_items_needed(L, P, W):
+    """Prefix and window items of a sequence of length L (brute force over its tokens):
+    each page meeting the prefix [0, min(P, L)) is one item, and each page meeting the
+    window's part past the prefix, [max(L - W, min(P, L)), L), is another."""
+    Pe = min(P, L)
+    w0 = max(L - W, Pe)
+    pre = {t // 16 for t in range(0, Pe)}
+    win = {t // 16 for t in range(w0, L)}
+    return len(pre) + len(win)
+
+
+@pytest.mark.parametrize("msl,P,W,budget", [
+    (249, 5, 231, 1),    # prefix end and window start on one page at every length: n_pages + 1 items
+    (241, 1, 228, 0),
+    (16 * 1024, 16 * 3 + 5, 16 * 1019, 2),   # prefix + window nearly cover 1024 pages
+    (16 * 1024, 16 * 1020 + 9, 40, 1),
+    (4000, 64, 256, 8), (65536, 128, 1024, 128), (3000, 300, 5000, 7)])
+def test_prefix_window_plan_holds_every_item(lib, msl, P, W, budget):
+    """The prefix/window workgroups the planner sizes from the host length bound hold
+    every prefix and window item of every length up to that bound (host only)."""
+    for B, hq, hkv in ((2, 8, 2), (16, 32, 8)):
+        n = (msl + 15) // 16
+        p = fsa.describe_step(fsa.dims(B, hq, hkv, 128, n, B * n), fsa.cfg(P, W, budget), msl)
+        if p["plan"] == "dense":
+            continue
+        cap = p["pw_workgroups"] * 16 * p["pw_items_per_wave"]
+        # every length for short bounds; otherwise the top 64 lengths (every residue of
+        # L mod 16 with the window past the prefix, where the count is largest)
+        lens = range(1, msl + 1) if msl <= 5000 else range(msl - 64, msl + 1)
+        need = max(_pw_items_needed(L, P, W) for L in lens)
+        assert cap >= need, (p, need)
+

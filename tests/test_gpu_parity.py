@@ -404,3 +404,61 @@ def test_validate_inputs_names_the_violation():
     bad_q.view(-1)[77] = float("nan")
     with pytest.raises(fsa.FsaError, match="q element 77"):
         fsa.validate_inputs(dw.dims, dw.max_seq_len, bad_q, dw.page_table, dw.seq_lens)
+    # before an append: the page table holds 256 pages (4096 tokens), so one
+    # more token for a full sequence overflows it, and the validator names it
+    cap = wl.max_pages * S
+    with pytest.raises(fsa.FsaError, match="sequence 0 overflows its page table"):
+        fsa.validate_inputs(dw.dims, cap, dw.q, dw.page_table, dw.seq_lens, n_new=1)
+    shorter = dw.seq_lens.clone()
+    shorter[0] = cap - 3
+    fsa.validate_inputs(dw.dims, cap, dw.q, dw.page_table, shorter, n_new=3)
+    with pytest.raises(fsa.FsaError, match="with 2 new tokens"):
+        fsa.validate_inputs(dw.dims, cap - 5, dw.q, dw.page_table, shorter, n_new=2)
+
+
+def test_append_at_page_table_capacity():
+    """An append that runs past a sequence's page table writes only the tokens
+    that have a page, and the length counts only those; the metadata still
+    equals a rebuild and the oracle's."""
+    wl = synth.workloads.build(name="capacity", seed=22, batch=2, hq=8, hkv=2, d=128, seq_lens=(4090, 100),
+                               prefix=32, window=128, budget=8, k_sigma=0.5, permuted=True)
+    assert wl.max_pages == 256
+    # sequence 1 gets its next page mapped (pool page ids past the generator's pool are
+    # not needed: its tokens 100..109 land on page 6, already mapped)
+    dw = DeviceWorkload(wl)
+    lens_out = torch.full_like(dw.seq_lens, -1)
+    kn, vn = _tokens_at(wl, wl.seq_lens, 10)
+    fsa.append_kv(dw.dims, 10, to_dev_bf16(kn), to_dev_bf16(vn), dw.page_table, dw.seq_lens, lens_out, dw.k_cache,
+                  dw.v_cache, dw.meta)
+    torch.cuda.synchronize()
+    assert lens_out.cpu().numpy().tolist() == [4096, 110]
+    for b, n_written in ((0, 6), (1, 10)):
+        for i in range(n_written):
+            t = int(wl.seq_lens[b]) + i
+            phys = wl.page_table[b, t // S]
+            wl.k_pool[phys, :, t % S, :] = kn[b, i]
+            wl.v_pool[phys, :, t % S, :] = vn[b, i]
+    wl.seq_lens = lens_out.cpu().numpy().astype(np.int32)
+    dw.seq_lens = lens_out
+    dw.max_seq_len = int(wl.seq_lens.max())
+    rebuilt = torch.zeros_like(dw.meta)
+    fsa.build_page_meta(dw.dims, dw.k_cache, dw.page_table, lens_out, rebuilt)
+    torch.cuda.synchronize()
+    assert torch.equal(rebuilt, dw.meta)
+    run_and_check(wl, dw=dw)
+
+
+@pytest.mark.parametrize("lens,cfg", [
+    ((249, 241), (5, 231, 1)),            # prefix end and window start share a page
+    ((241, 236), (1, 228, 0)),
+    ((16384, 16379), (53, 16304, 1)),     # prefix + window cover all but two pages of 1024
+    ((16384, 16000), (53, 16304, 0)),
+    ((16384, 9000), (16 * 1020 + 9, 40, 1))])
+def test_prefix_and_window_nearly_cover_the_sequence(lens, cfg):
+    """Prefix and window cover all but one or two pages, with a shorter sequence in
+    the batch: every prefix and window item is attended (the planner sizes the
+    prefix/window workgroups for one item more than the pages when the prefix
+    ends and the window starts on the same page)."""
+    wl = synth.workloads.build(name="nearcover", seed=23, batch=2, hq=8, hkv=2, d=64, seq_lens=lens,
+                               prefix=cfg[0], window=cfg[1], budget=cfg[2], k_sigma=0.5, permuted=True)
+    run_and_check(wl)
