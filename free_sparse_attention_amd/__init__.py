@@ -26,6 +26,8 @@ from ._lib import (  # noqa: F401
     read_probe,
     select_pages,
     sparse_decode_attn,
+    sparse_decode_attn_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     sparse_decode_workspace_bytes,
     validate_inputs,
 )

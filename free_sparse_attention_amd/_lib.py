@@ -23,7 +23,7 @@ EXPORTED = (
     "fsa_quest_scores", "fsa_max_work_items", "fsa_select_pages",
     "fsa_sparse_decode_workspace_bytes", "fsa_sparse_decode_attn",
     "fsa_dense_decode_workspace_bytes", "fsa_dense_decode_attn", "fsa_validate_inputs", "fsa_describe_step",
-    "fsa_append_decode_attn", "fsa_device_memory", "fsa_read_probe",
+    "fsa_append_decode_attn", "fsa_device_memory", "fsa_read_probe", "fsa_sparse_decode_attn_noalloc",
 )
 
 
@@ -71,6 +71,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             "fsa_select_pages": (i32, [D, C, i32, vp, vp, vp, vp, vp, vp, vp]),
             "fsa_sparse_decode_workspace_bytes": (sz, [D, C, i32]),
             "fsa_sparse_decode_attn": (i32, [D, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "fsa_sparse_decode_attn_noalloc": (i32, [D, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "fsa_dense_decode_workspace_bytes": (sz, [D, i32]),
             "fsa_dense_decode_attn": (i32, [D, f32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "fsa_validate_inputs": (i32, [D, i32, i32, vp, vp, vp, vp, vp]),
@@ -217,6 +218,18 @@ def sparse_decode_attn(d: Dims, c: LayerCfg, sm_scale, max_seq_len, q, k_cache, 
         _p(v_cache, "v_cache", 2), _p(meta, "meta", 2), _i32(page_table, "page_table"),
         _i32(seq_lens, "seq_lens"), _p(out, "out", 2), _i32(sel_pages, "sel_pages"),
         _p(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # FSA_NOALLOC_SCRATCH_BYTES in include/fsa.h
+
+
+def sparse_decode_attn_noalloc(d: Dims, c: LayerCfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table,
+                               seq_lens, out, sel_pages, stream=None):
+    """fsa_sparse_decode_attn with the library's own per-GPU workspace (no allocation)."""
+    _check(load().fsa_sparse_decode_attn_noalloc(
+        ctypes.byref(d), c, float(sm_scale), int(max_seq_len), _p(q, "q", 2), _p(k_cache, "k_cache", 2),
+        _p(v_cache, "v_cache", 2), _p(meta, "meta", 2), _i32(page_table, "page_table"),
+        _i32(seq_lens, "seq_lens"), _p(out, "out", 2), _i32(sel_pages, "sel_pages"), _stream(stream)))
 
 
 def append_decode_attn(d: Dims, n_new, k_new, v_new, seq_lens, seq_lens_out, c: LayerCfg, sm_scale, max_seq_len,

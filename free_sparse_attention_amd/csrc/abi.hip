@@ -4,6 +4,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "../../include/fsa.h"
@@ -419,6 +420,32 @@ fsa_status run_sparse_step(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_sca
   return hip_status(fsa::launch_attention(fsa::kList, w.plan, a, st), "decode attention launch");
 }
 
+// ---------------------------------------------------------------- allocation-free step
+// Workspace of fsa_sparse_decode_attn_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  In host code its name is only a
+// host-side stand-in, never a device address: the address of each GPU's copy
+// is looked up once per device (with that device current) and kept here.
+static __device__ __align__(256) uint8_t scratch[FSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+fsa_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  FSA_CHECK(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FSA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    FSA_CHECK(hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (!p) return fail(FSA_ERR_HIP, "hipGetSymbolAddress(scratch) gave no address");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return FSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -432,6 +459,24 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
                        workspace, workspace_bytes));
   return run_sparse_step(dims, cfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table, seq_lens, out,
                          sel_pages, workspace, static_cast<hipStream_t>(stream), nullptr);
+}
+
+fsa_status fsa_sparse_decode_attn_noalloc(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_scale,
+                                          int32_t max_seq_len, const void* q, const void* k_cache,
+                                          const void* v_cache, const void* meta, const int32_t* page_table,
+                                          const int32_t* seq_lens, void* out, int32_t* sel_pages, void* stream) {
+  // every host check, the size limit included, before any HIP call
+  FSA_CHECK(check_step_args(dims, cfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table, seq_lens, out));
+  const size_t total = sparse_ws(dims, cfg, max_seq_len).total;
+  if (total > (size_t)FSA_NOALLOC_SCRATCH_BYTES)
+    return fail(FSA_ERR_WORKSPACE,
+                "this step needs %zu bytes of workspace; the allocation-free call holds at most %zu "
+                "(use fsa_sparse_decode_attn with a caller-owned workspace)",
+                total, (size_t)FSA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  FSA_CHECK(scratch_of_current_device(&ws));
+  return run_sparse_step(dims, cfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table, seq_lens, out,
+                         sel_pages, ws, static_cast<hipStream_t>(stream), nullptr);
 }
 
 fsa_status fsa_append_decode_attn(const fsa_dims* dims, int32_t n_new, const void* k_new, const void* v_new,

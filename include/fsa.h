@@ -209,6 +209,28 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
                                   const int32_t* seq_lens, void* out, int32_t* sel_pages,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes the allocation-free decode step holds per GPU. */
+#define FSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* fsa_sparse_decode_attn without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The caller still passes every
+ * input and output; the step's workspace (scores, selected items, split
+ * partials) is a device array inside the library of FSA_NOALLOC_SCRATCH_BYTES
+ * bytes, one per GPU, held until the process ends.  The call allocates
+ * nothing; its first call on a device looks up that device's copy of the
+ * array.  Steps whose workspace (fsa_sparse_decode_workspace_bytes) exceeds
+ * the array return FSA_ERR_WORKSPACE before any HIP call.  Every call on one
+ * GPU shares that GPU's array: calls that may overlap (different streams, or
+ * several threads) race and must be ordered by the caller.  The array needs
+ * no initial contents.  Arguments and results otherwise as in
+ * fsa_sparse_decode_attn, whose kernels it runs: the results are the same
+ * bit for bit. */
+fsa_status fsa_sparse_decode_attn_noalloc(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_scale,
+                                          int32_t max_seq_len, const void* q, const void* k_cache,
+                                          const void* v_cache, const void* meta, const int32_t* page_table,
+                                          const int32_t* seq_lens, void* out, int32_t* sel_pages, void* stream);
+
 /* How fsa_sparse_decode_attn will run a step of these shapes on the current
  * device (host only: no device memory is touched; queries the device's
  * compute-unit count, 256 when there is no device).  Writes up to n_info of:

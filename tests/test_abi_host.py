@@ -189,3 +189,27 @@ def test_prefix_window_plan_holds_every_item(lib, msl, P, W, budget):
         need = max(_pw_items_needed(L, P, W) for L in lens)
         assert cap >= need, (p, need)
 
+
+def test_noalloc_step_checks_size_before_any_device_call(lib):
+    """The allocation-free step rejects a step whose workspace exceeds its fixed
+    scratch, and bad arguments, before any HIP call (so this runs without a GPU)."""
+    p = ctypes.c_void_p(16)  # never dereferenced
+    d = fsa.dims(64, 64, 8, 128, 32768, 64 * 32768)
+    c = fsa.cfg(128, 1024, 128)
+    assert fsa.sparse_decode_workspace_bytes(d, c, 32768 * 16) > fsa.NOALLOC_SCRATCH_BYTES
+    st = lib.fsa_sparse_decode_attn_noalloc(ctypes.byref(d), c, 0.1, 32768 * 16, p, p, p, p, p, p, p, None, None)
+    assert st == _lib.FSA_ERR_WORKSPACE and b"allocation-free" in lib.fsa_last_error()
+    small = _d()
+    for args, status in (((fsa.cfg(0, 0, 0), 0.1, 4096), _lib.FSA_ERR_INVALID_ARG),
+                         ((fsa.cfg(64, 256, 32), 0.0, 4096), _lib.FSA_ERR_INVALID_ARG),
+                         ((fsa.cfg(64, 256, 32), 0.1, 4097), _lib.FSA_ERR_INVALID_ARG)):
+        assert lib.fsa_sparse_decode_attn_noalloc(ctypes.byref(small), *args, p, p, p, p, p, p, p, None,
+                                                  None) == status
+    assert lib.fsa_sparse_decode_attn_noalloc(ctypes.byref(small), fsa.cfg(64, 256, 32), 0.1, 4096, p, p, p, None,
+                                              p, p, p, None, None) == _lib.FSA_ERR_INVALID_ARG
+    # the sizes the decode workloads need fit
+    for B, hq, hkv, L, cfg in ((4, 16, 4, 65536, (128, 1024, 128)), (4, 32, 4, 262144, (128, 4096, 256)),
+                               (16, 32, 8, 262144 + 64, (128, 2048, 256))):
+        n = (L + 15) // 16
+        assert fsa.sparse_decode_workspace_bytes(fsa.dims(B, hq, hkv, 128, n, B * n), fsa.cfg(*cfg), L) <= \
+            fsa.NOALLOC_SCRATCH_BYTES
