@@ -95,16 +95,20 @@ __device__ __forceinline__ void attend_items(const uint16_t* __restrict__ kc, co
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(st.m, mx);
     const float alpha = exp2f(st.m - m_new);
-    float p[4], psum = 0.f;
+    // The weights are rounded to bf16 for the P.V product, and the sum l adds
+    // the same rounded weights: numerator and denominator use one set of
+    // weights, so the output is a convex combination of the values.
+    uint32_t pr[4];
+    float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p[r] = exp2f(x[r] - m_new);
-      psum += p[r];
+      pr[r] = f32_to_bf16_bits(exp2f(x[r] - m_new));
+      psum += __uint_as_float(pr[r] << 16);
     }
     st.l = st.l * alpha + psum;
     st.m = m_new;
-    const uint32_t p01 = f32_to_bf16_bits(p[0]) | (f32_to_bf16_bits(p[1]) << 16);
-    const uint32_t p23 = f32_to_bf16_bits(p[2]) | (f32_to_bf16_bits(p[3]) << 16);
+    const uint32_t p01 = pr[0] | (pr[1] << 16);
+    const uint32_t p23 = pr[2] | (pr[3] << 16);
     const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
 #pragma unroll
     for (int t = 0; t < NDT; ++t) {
