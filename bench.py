@@ -58,16 +58,65 @@ def alg_bytes(wl):
     return score, step
 
 
-def measured_traffic(kernel_source: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, or None when
-    the kernel source has changed since the counters were taken."""
+def unit_sizes(wl):
+    """Per sequence b: (L, n pages, C candidates, k selected, prefix+window tokens, selected middle tokens)."""
+    S = wl.page
+    P, W, budget = wl.cfg
+    rows = []
+    for b in range(wl.batch):
+        L = int(wl.seq_lens[b])
+        Pe, Ws = min(P, L), max(0, L - W)
+        C = (-(-Ws // S) - Pe // S) if Pe < Ws else 0
+        k = min(budget, C)
+        pw = Pe + (L - max(Ws, Pe))
+        mid = min(k * S, max(0, Ws - Pe))
+        rows.append((L, -(-L // S), C, k, pw, mid))
+    return rows
+
+
+LAUNCHES = {"wide": ("quest_score_kernel", "select_attend_kernel", "combine_kernel"),
+            "narrow": ("quest_score_kernel", "select_attend_kernel", "decode_attention_kernel", "combine_kernel"),
+            "dense": ("decode_attention_kernel", "combine_kernel")}
+
+
+def launch_bytes(wl, plan):
+    """Algorithmic HBM bytes of each launch of one step, in launch order.
+
+    Per (sequence, KV head) unit: the scoring launch reads the candidates'
+    metadata 4 D C and the group's queries 2 G D; the attention reads the K/V
+    of its tokens, 4 D per token, and the sequence's page-table entries (4 n
+    per sequence, charged to the launch that first reads them); the combine
+    writes the output 2 G D.  Intermediate traffic (scores, partial results)
+    is not counted."""
+    D, G, hkv = wl.d, wl.group, wl.hkv
+    rows = unit_sizes(wl)
+    meta = sum(hkv * 4 * D * C for _, _, C, _, _, _ in rows)
+    q = wl.batch * hkv * 2 * G * D
+    out = q
+    pt = sum(4 * n for _, n, _, _, _, _ in rows)
+    kv_pw = sum(hkv * 4 * D * pw for _, _, _, _, pw, _ in rows)
+    kv_sel = sum(hkv * 4 * D * mid for _, _, _, _, _, mid in rows)
+    if plan == "wide":
+        return [meta + q, kv_pw + kv_sel + pt, out]
+    if plan == "narrow":
+        return [meta + q, kv_pw + pt, kv_sel, out]
+    kv_all = sum(hkv * 4 * D * L for L, _, _, _, _, _ in rows)
+    return [kv_all + pt + q, out]
+
+
+def measured_traffic(kernel: str, sources, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter runs
+    (profiles/<kernel>_<workload>_counters.json), or None when any of its
+    sources has changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "quest_score_%s_counters.json" % workload)
+    path = os.path.join(ROOT, "profiles", "%s_%s_counters.json" % (kernel, workload))
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, kernel_source), "rb").read()
-    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+    h = hashlib.sha256()
+    for f in sources:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec.get("sources_sha256"):
         return None
     return rec["hbm_bytes_per_launch"]
 
@@ -114,100 +163,35 @@ def hbm_ceiling(reps=20, nbytes=2 << 30):
             "read_ceiling_GBps": nbytes / (ms * 1e-3) / 1e9, "read_probe_bytes": nbytes, "device": props}
 
 
-def cpu_baseline(wl, budget_s=12.0):
-    """The CPU oracle timed on host cores over a bounded sample of units of the same workload."""
+def cpu_baseline(wl, budget_s=8.0):
+    """The plain C++ oracle timed on the host's cores over a bounded sample of
+    steps of the same workload: first on one thread, then with its units
+    spread over every host CPU (std::thread).  Page metadata is built once
+    beforehand (on the GPU it is kept current by the append, not rebuilt per
+    step), so a timed step is what the GPU step does: score the candidates,
+    select, merge, attend."""
     import oracle
-    from threadpoolctl import threadpool_limits
 
-    S = wl.page
-    P, W, budget = wl.cfg
     units = [(b, g) for b in range(wl.batch) for g in range(wl.hkv)]
-    prepared = []
-    for b, g in units:  # gather and page metadata are prefill-side: outside the timed region
-        q, K, V = oracle.unit_inputs(wl, b, g)
-        m, M = oracle.page_minmax(K, S)
-        prepared.append((b, q, K, V, m, M))
-    done = 0
-    t_total = 0.0
-    with threadpool_limits(limits=1):
-        while t_total < budget_s:
-            b, q, K, V, m, M = prepared[done % len(prepared)]
-            L = int(wl.seq_lens[b])
-            t0 = time.perf_counter()
-            cand = oracle.candidate_pages(L, P, W, S)
-            s = oracle.group_score(oracle.quest_bound(q, m[cand], M[cand]))
-            sel = oracle.select_topk(s, cand, budget)
-            mask = oracle.attended_mask(L, P, W, S, sel)
-            oracle.attend(q, K, V, mask, wl.sm_scale)
-            t_total += time.perf_counter() - t0
-            done += 1
-    steps = done / len(units)
-    return {"value": steps / t_total, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "us_per_step": 1e6 * t_total / steps, "GBps": alg_bytes(wl)[1] * steps / t_total / 1e9,
-            "host": host_cpu(),
-            "sample": f"{done} (sequence, KV head) units of the {wl.name} step ({steps:.2f} steps) scored, "
-                      f"selected and attended by the float64 numpy oracle on 1 host thread, "
-                      f"{t_total:.1f} s; page metadata precomputed"}
-
-
-_PAR_UNITS = None  # prepared oracle units, inherited by the forked workers below
-
-
-def _oracle_unit(wl, prep):
-    import oracle
-
-    b, q, K, V, m, M = prep
-    P, W, budget = wl.cfg
-    L = int(wl.seq_lens[b])
-    cand = oracle.candidate_pages(L, P, W, wl.page)
-    s = oracle.group_score(oracle.quest_bound(q, m[cand], M[cand]))
-    sel = oracle.select_topk(s, cand, budget)
-    mask = oracle.attended_mask(L, P, W, wl.page, sel)
-    oracle.attend(q, K, V, mask, wl.sm_scale)
-
-
-def _par_worker(arg):
-    from threadpoolctl import threadpool_limits
-
-    idx, n_workers, budget_s = arg
-    wl, prepared = _PAR_UNITS
-    done = 0
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
+    nproc = os.cpu_count() or 1
+    meta = oracle.build_meta_all(wl, nthreads=nproc)
+    step_bytes = alg_bytes(wl)[1]
+    res = {}
+    for threads in (1, nproc):
+        done, t0 = 0, time.perf_counter()
         while time.perf_counter() - t0 < budget_s:
-            _oracle_unit(wl, prepared[(idx + done * n_workers) % len(prepared)])
+            oracle.decode_units(wl, units, meta=meta, nthreads=threads)
             done += 1
-    return done
-
-
-def cpu_baseline_parallel(wl, workers=16, budget_s=10.0):
-    """The same oracle over independent (sequence, KV head) units in `workers`
-    forked processes (one thread each).  Runs before the process touches the
-    GPU: the workers are plain forks doing numpy work only."""
-    import multiprocessing as mp
-
-    import oracle
-
-    global _PAR_UNITS
-    prepared = []
-    for b in range(wl.batch):
-        for g in range(wl.hkv):
-            q, K, V = oracle.unit_inputs(wl, b, g)
-            m, M = oracle.page_minmax(K, wl.page)
-            prepared.append((b, q, K, V, m, M))
-    _PAR_UNITS = (wl, prepared)
-    ctx = mp.get_context("fork")
-    t0 = time.perf_counter()
-    with ctx.Pool(workers) as pool:
-        done = sum(pool.map(_par_worker, [(i, workers, budget_s) for i in range(workers)]))
-    wall = time.perf_counter() - t0
-    _PAR_UNITS = None
-    steps = done / len(prepared)
-    return {"value": steps / wall, "unit": "steps/s", "cores": workers, "kind": "oracle",
-            "us_per_step": 1e6 * wall / steps, "GBps": alg_bytes(wl)[1] * steps / wall / 1e9,
-            "sample": f"{done} (sequence, KV head) units of the {wl.name} step ({steps:.2f} steps) by the float64 "
-                      f"numpy oracle in {workers} processes of one thread each, {wall:.1f} s wall; "
-                      f"page metadata precomputed"}
+        wall = time.perf_counter() - t0
+        res[threads] = {"value": done / wall, "unit": "steps/s", "cores": threads, "kind": "oracle",
+                        "us_per_step": 1e6 * wall / done, "GBps": step_bytes * done / wall / 1e9,
+                        "sample": f"{done} whole {wl.name} steps ({len(units)} (sequence, KV head) units each) "
+                                  f"by the plain C++ oracle (double accumulation) on {threads} host thread(s), "
+                                  f"{wall:.1f} s wall; page metadata built beforehand"}
+    best = dict(res[nproc])
+    best["single_thread"] = res[1]
+    best["host"] = host_cpu()
+    return best
 
 
 def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
@@ -282,7 +266,32 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
     n_k = reps_kernel or max(steps, 50)
     ms_score = timed(score, n_k, 10)
 
+    # each launch of the step timed live with HIP events on the step's
+    # stream, in its place in the step: the prefix of launches 0..j is timed
+    # over `steps` rotated steps, and launch j is charged the difference
+    # between prefixes j and j - 1 (so the launches add up to the step)
+    plan = fsa.describe_step(base.dims, c, msl)["plan"]
+    names = LAUNCHES[plan]
+    step(0)
+
+    def prefix_fn(j):
+        def run(i):
+            k, v, m = reps[i % R]
+            return fsa.sparse_decode_attn_launches(base.dims, c, wl.sm_scale, msl, base.q, k, v, m, base.page_table,
+                                                   base.seq_lens, out, None, ws, 0, j, stream)
+        return run
+
+    assert prefix_fn(0)(0) == len(names), (plan, names)
+    pre = [timed(prefix_fn(j), steps, min(warmup, 10)) for j in range(len(names))]
+    per = [pre[0]] + [max(1e-6, pre[j] - pre[j - 1]) for j in range(1, len(names))]
+    lb = launch_bytes(wl, plan)
+    launches = [{"kernel": names[j], "avg_launch_us": 1000.0 * per[j], "alg_bytes": lb[j],
+                 "achieved_GBps": lb[j] / (per[j] * 1e-3) / 1e9, "frac": lb[j] / (per[j] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "time_share": per[j] / sum(per)} for j in range(len(names))]
+    marked_ms = sum(per)
+
     res = {"ms_per_step": ms_step, "steps_per_s": 1000.0 / ms_step, "step_alg_bytes": step_bytes,
+           "plan": plan, "launches": launches, "sum_of_launches_us": 1000.0 * marked_ms,
            "step_GBps": step_bytes / (ms_step * 1e-3) / 1e9, "score_ms": ms_score,
            "score_alg_bytes": score_bytes, "score_GBps": score_bytes / (ms_score * 1e-3) / 1e9,
            "replicas": R, "warm_mall_step_us": 1000.0 * warm_ms,
@@ -347,10 +356,9 @@ CALIB_CFGS = ((128, 1024, 64), (128, 1024, 256), (128, 1024, 1024), (128, 4096, 
               (128, 4096, 1024))
 
 
-def calibrate(steps, warmup):
-    """Step times over a grid of context lengths, query-group sizes and layer
-    configurations (prefix, window, budget), batch 4, Hkv 4, D 128: the data
-    the per-layer decode-cost model is fitted to."""
+def _time_points(groups, steps, warmup, tag):
+    """Sparse and dense step times, batch 4, Hkv 4, D 128, for every
+    (G, L, [layer configurations]) group: the data of the decode-cost model."""
     import torch
 
     import free_sparse_attention_amd as fsa
@@ -358,45 +366,61 @@ def calibrate(steps, warmup):
     from tests.gpu_harness import DeviceWorkload
 
     rows = []
-    for G in CALIB_GROUPS:
-        for L in CALIB_LENS:
-            wl = synth.make_workload("ctx64k", seq_lens=(L,) * 4, hq=4 * G)
-            base = DeviceWorkload(wl)
-            R = 3
-            reps = [(base.k_cache, base.v_cache, base.meta)] + [
-                (base.k_cache.clone(), base.v_cache.clone(), base.meta.clone()) for _ in range(R - 1)]
-            out = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.bfloat16, device="cuda")
-            stream = torch.cuda.current_stream()
+    for G, L, cfgs in groups:
+        wl = synth.make_workload("ctx64k", seq_lens=(L,) * 4, hq=4 * G)
+        base = DeviceWorkload(wl)
+        R = 3
+        reps = [(base.k_cache, base.v_cache, base.meta)] + [
+            (base.k_cache.clone(), base.v_cache.clone(), base.meta.clone()) for _ in range(R - 1)]
+        out = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.bfloat16, device="cuda")
+        stream = torch.cuda.current_stream()
 
-            def timed(fn, n, w):
-                for i in range(w):
-                    fn(i)
-                torch.cuda.synchronize()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for i in range(n):
-                    fn(w + i)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                return 1000.0 * e0.elapsed_time(e1) / n
+        def timed(fn, n, w):
+            for i in range(w):
+                fn(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(n):
+                fn(w + i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return 1000.0 * e0.elapsed_time(e1) / n
 
-            dws = base.dense_workspace()
-            dense_us = timed(lambda i: fsa.dense_decode_attn(base.dims, wl.sm_scale, L, base.q, reps[i % R][0],
-                                                             reps[i % R][1], base.page_table, base.seq_lens, out,
-                                                             dws, stream), max(10, steps // 4), 3)
-            for cfg in CALIB_CFGS:
-                c = fsa.cfg(*cfg)
-                ws = base.workspace(cfg=cfg)
-                us = timed(lambda i: fsa.sparse_decode_attn(base.dims, c, wl.sm_scale, L, base.q, reps[i % R][0],
-                                                            reps[i % R][1], reps[i % R][2], base.page_table,
-                                                            base.seq_lens, out, None, ws, stream), steps, warmup)
-                rows.append({"batch": 4, "q_heads": 4 * G, "kv_heads": 4, "head_dim": 128, "seq_len": L,
-                             "prefix": cfg[0], "window": cfg[1], "budget_pages": cfg[2], "sparse_us": us,
-                             "dense_us": dense_us})
-                log(f"[calibrate] G={G} L={L} cfg={cfg}: sparse {us:.1f} us, dense {dense_us:.1f} us")
-            del reps, base, wl
-            torch.cuda.empty_cache()
+        dws = base.dense_workspace()
+        dense_us = timed(lambda i: fsa.dense_decode_attn(base.dims, wl.sm_scale, L, base.q, reps[i % R][0],
+                                                         reps[i % R][1], base.page_table, base.seq_lens, out,
+                                                         dws, stream), max(10, steps // 4), 3)
+        for cfg in cfgs:
+            c = fsa.cfg(*cfg)
+            ws = base.workspace(cfg=cfg)
+            us = timed(lambda i: fsa.sparse_decode_attn(base.dims, c, wl.sm_scale, L, base.q, reps[i % R][0],
+                                                        reps[i % R][1], reps[i % R][2], base.page_table,
+                                                        base.seq_lens, out, None, ws, stream), steps, warmup)
+            rows.append({"batch": 4, "q_heads": 4 * G, "kv_heads": 4, "head_dim": 128, "seq_len": L,
+                         "prefix": cfg[0], "window": cfg[1], "budget_pages": cfg[2], "sparse_us": us,
+                         "dense_us": dense_us})
+            log(f"[{tag}] G={G} L={L} cfg={cfg}: sparse {us:.1f} us, dense {dense_us:.1f} us")
+        del reps, base, wl
+        torch.cuda.empty_cache()
     return rows
+
+
+def calibrate(steps, warmup):
+    """Step times over a grid of context lengths, query-group sizes and layer
+    configurations (prefix, window, budget), batch 4, Hkv 4, D 128: the data
+    the per-layer decode-cost model is fitted to."""
+    return _time_points([(G, L, CALIB_CFGS) for G in CALIB_GROUPS for L in CALIB_LENS], steps, warmup, "calibrate")
+
+
+def holdout(steps, warmup):
+    """Points the decode-cost model is not fitted to: the 12 layer
+    configurations of the 12-layer sweep at 128k (G 4), and G 8 with a 2048
+    window at lengths and budgets outside the calibration grid."""
+    import synth
+    sweep = [synth.workloads.sweep_layer_cfg(3, layer) for layer in range(12)]
+    g8 = [(128, 2048, b) for b in (128, 384)]
+    return _time_points([(4, 131072, sweep), (8, 49152, g8), (8, 163840, g8)], steps, warmup, "holdout")
 
 
 def layers12(steps, warmup):
@@ -562,7 +586,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="ctx64k", help="tiny, ctx64k or ctx256k")
-    ap.add_argument("--no-also", action="store_true", help="skip the 256k measurement")
+    ap.add_argument("--no-also", action="store_true", help="skip the 256k and ragged serving measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--sweep", action="store_true",
@@ -573,17 +597,15 @@ def main():
                     help="instead: 12-layer model step (append + decode per layer), eager and as a HIP graph")
     ap.add_argument("--calibrate", action="store_true",
                     help="instead: step times over a grid of lengths, group sizes and layer configurations")
+    ap.add_argument("--holdout", action="store_true",
+                    help="instead: step times at layer configurations outside the calibration grid")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU; this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: nothing here runs on more than one (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import synth
     synth.lib()
-    par = None
-    if not (args.ragged or args.layers12 or args.calibrate or args.sweep or args.no_cpu_baseline):
-        # oracle in parallel processes first, while this process has not touched the GPU
-        par = cpu_baseline_parallel(synth.make_workload(args.workload))
     import free_sparse_attention_amd as fsa
     fsa.load()
 
@@ -605,10 +627,12 @@ def main():
                           "result": r}), flush=True)
         return
 
-    if args.calibrate:
-        rows = calibrate(max(20, args.steps // 4), args.warmup)
+    if args.calibrate or args.holdout:
+        rows = (calibrate if args.calibrate else holdout)(max(20, args.steps // 4), args.warmup)
         print(json.dumps({"metric": "decode step time over layer configurations", "unit": "us", "n_gpus": 1,
-                          "data": "synthetic (seeded)", "rows": rows}), flush=True)
+                          "data": "synthetic (seeded)", "compute_units": 256,
+                          "command": "python bench.py " + ("--calibrate" if args.calibrate else "--holdout"),
+                          "rows": rows}), flush=True)
         return
 
     if args.sweep:
@@ -628,7 +652,10 @@ def main():
                  "prefix": wl.cfg[0], "window": wl.cfg[1], "budget_pages": wl.cfg[2],
                  "page_table": "permuted" if wl.permuted else "contiguous"}
     main_res = measure(wl, args.steps, args.warmup, with_dense=not args.no_dense)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline: the C++ oracle on the host")
+        cpu = cpu_baseline(wl)
     del wl
     hbm = hbm_ceiling()
 
@@ -637,8 +664,17 @@ def main():
         wl2 = synth.make_workload("ctx256k")
         also["ctx256k"] = measure(wl2, max(20, args.steps // 2), args.warmup, with_dense=not args.no_dense)
         del wl2
+    if not args.no_also:
+        log("[bench] ragged16 serving step")
+        also["ragged16"] = ragged_serving(max(20, args.steps // 4), 4)
 
     r = main_res
+    top = max(r["launches"], key=lambda x: x["avg_launch_us"])
+    src = {"quest_score_kernel": ["free_sparse_attention_amd/csrc/quest_score.hip",
+                                  "free_sparse_attention_amd/csrc/append_core.h"],
+           "select_attend_kernel": ["free_sparse_attention_amd/csrc/select_pages.hip",
+                                    "free_sparse_attention_amd/csrc/select_core.h",
+                                    "free_sparse_attention_amd/csrc/attend_core.h"]}.get(top["kernel"])
     line = {
         "metric": "sparse decode-attn steps/sec + achieved HBM GB/s (% peak) at 64k/256k ctx",
         "value": r["steps_per_s"], "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
@@ -648,27 +684,37 @@ def main():
         "config": wl_config,
         "achieved_GBps": r["step_GBps"], "pct_hbm_peak": 100.0 * r["step_GBps"] / HBM_PEAK_GBS,
         "speedup_vs_dense": r.get("speedup_vs_dense"),
-        "roofline": {"bound": "hbm", "kernel": "quest_score_kernel", "achieved": r["score_GBps"],
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": r["score_GBps"] / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("free_sparse_attention_amd/csrc/quest_score.hip", args.workload),
-                     "avg_launch_us": 1000.0 * r["score_ms"],
-                     "alg_bytes_per_launch": r["score_alg_bytes"],
-                     "frac_of_read_ceiling": r["score_GBps"] / hbm["read_ceiling_GBps"]},
+        "roofline": {"bound": "hbm", "kernel": top["kernel"], "achieved": top["achieved_GBps"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": top["frac"],
+                     "traffic": measured_traffic(top["kernel"], src, args.workload) if src else None,
+                     "avg_launch_us": top["avg_launch_us"], "alg_bytes_per_launch": top["alg_bytes"],
+                     "time_share": top["time_share"],
+                     "frac_of_read_ceiling": top["achieved_GBps"] / hbm["read_ceiling_GBps"],
+                     "launches": r["launches"],
+                     "whole_step": {"achieved": r["step_GBps"], "frac": r["step_GBps"] / HBM_PEAK_GBS,
+                                    "alg_bytes": r["step_alg_bytes"]}},
         "hbm_peak": hbm,
         "pct_of_read_ceiling": 100.0 * r["step_GBps"] / hbm["read_ceiling_GBps"],
         "warm_mall_step_us": r["warm_mall_step_us"],
         "cpu_baseline": cpu,
-        "cpu_baseline_parallel": par,
         "repetitions": r["repetitions"],
         "cold_single_step_us": r["cold_single_step_us"],
-        "also": {k: {"steps_per_s": v["steps_per_s"], "ms_per_step": v["ms_per_step"],
-                     "achieved_GBps": v["step_GBps"], "pct_hbm_peak": 100.0 * v["step_GBps"] / HBM_PEAK_GBS,
-                     "speedup_vs_dense": v.get("speedup_vs_dense"), "score_GBps": v["score_GBps"],
-                     "score_us": 1000.0 * v["score_ms"], "warm_mall_step_us": v["warm_mall_step_us"],
-                     "repetitions": v["repetitions"],
-                     "cold_single_step_us": v["cold_single_step_us"]} for k, v in also.items()},
+        "also": {},
         "detail": {k: v for k, v in r.items()},
     }
+    for k, v in also.items():
+        if k == "ragged16":
+            line["also"][k] = {"steps_per_s": v["steps_per_s"], "us_per_step": v["us_per_step"],
+                               "achieved_GBps": v["step_GBps"], "pct_hbm_peak": 100.0 * v["step_GBps"] / HBM_PEAK_GBS,
+                               "speedup_vs_dense": v["speedup_vs_dense"], "step": "one-token append + sparse decode",
+                               "detail": v}
+        else:
+            line["also"][k] = {"steps_per_s": v["steps_per_s"], "ms_per_step": v["ms_per_step"],
+                               "achieved_GBps": v["step_GBps"], "pct_hbm_peak": 100.0 * v["step_GBps"] / HBM_PEAK_GBS,
+                               "speedup_vs_dense": v.get("speedup_vs_dense"), "plan": v["plan"],
+                               "launches": v["launches"], "score_GBps": v["score_GBps"],
+                               "warm_mall_step_us": v["warm_mall_step_us"], "repetitions": v["repetitions"],
+                               "cold_single_step_us": v["cold_single_step_us"]}
     print(json.dumps(line), flush=True)
 
 

@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     select_pages,
     sparse_decode_attn,
     sparse_decode_attn_noalloc,
+    sparse_decode_attn_launches,
     NOALLOC_SCRATCH_BYTES,
     sparse_decode_workspace_bytes,
     validate_inputs,

@@ -24,6 +24,7 @@ EXPORTED = (
     "fsa_sparse_decode_workspace_bytes", "fsa_sparse_decode_attn",
     "fsa_dense_decode_workspace_bytes", "fsa_dense_decode_attn", "fsa_validate_inputs", "fsa_describe_step",
     "fsa_append_decode_attn", "fsa_device_memory", "fsa_read_probe", "fsa_sparse_decode_attn_noalloc",
+    "fsa_sparse_decode_attn_launches",
 )
 
 
@@ -72,6 +73,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             "fsa_sparse_decode_workspace_bytes": (sz, [D, C, i32]),
             "fsa_sparse_decode_attn": (i32, [D, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "fsa_sparse_decode_attn_noalloc": (i32, [D, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+            "fsa_sparse_decode_attn_launches": (i32, [D, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, i32,
+                                                      vp]),
             "fsa_dense_decode_workspace_bytes": (sz, [D, i32]),
             "fsa_dense_decode_attn": (i32, [D, f32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "fsa_validate_inputs": (i32, [D, i32, i32, vp, vp, vp, vp, vp]),
@@ -230,6 +233,20 @@ def sparse_decode_attn_noalloc(d: Dims, c: LayerCfg, sm_scale, max_seq_len, q, k
         ctypes.byref(d), c, float(sm_scale), int(max_seq_len), _p(q, "q", 2), _p(k_cache, "k_cache", 2),
         _p(v_cache, "v_cache", 2), _p(meta, "meta", 2), _i32(page_table, "page_table"),
         _i32(seq_lens, "seq_lens"), _p(out, "out", 2), _i32(sel_pages, "sel_pages"), _stream(stream)))
+
+
+def sparse_decode_attn_launches(d: Dims, c: LayerCfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table,
+                                seq_lens, out, sel_pages, workspace, first, last, stream=None) -> int:
+    """Only launches first..last of the decode step (measurement); returns the step's launch count."""
+    n = load().fsa_sparse_decode_attn_launches(
+        ctypes.byref(d), c, float(sm_scale), int(max_seq_len), _p(q, "q", 2), _p(k_cache, "k_cache", 2),
+        _p(v_cache, "v_cache", 2), _p(meta, "meta", 2), _i32(page_table, "page_table"),
+        _i32(seq_lens, "seq_lens"), _p(out, "out", 2), _i32(sel_pages, "sel_pages"),
+        _p(workspace, "workspace"), workspace.numel() * workspace.element_size(), int(first), int(last),
+        _stream(stream))
+    if n < 0:
+        raise FsaError(FSA_ERR_INVALID_ARG, load().fsa_last_error().decode())
+    return n
 
 
 def append_decode_attn(d: Dims, n_new, k_new, v_new, seq_lens, seq_lens_out, c: LayerCfg, sm_scale, max_seq_len,

@@ -7,8 +7,8 @@
 #include <mutex>
 #include <string>
 
-#include "../../include/fsa.h"
-#include "../../include/fsa_measure.h"
+#include "fsa.h"
+#include "fsa_measure.h"
 #include "append_core.h"
 
 namespace {
@@ -346,13 +346,16 @@ fsa_status check_step(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_scale, i
 fsa_status run_sparse_step(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_scale, int32_t max_seq_len,
                            const void* q, const void* k_cache, const void* v_cache, const void* meta,
                            const int32_t* page_table, const int32_t* seq_lens, void* out, int32_t* sel_pages,
-                           void* workspace, hipStream_t st, const fsa::AppendArgs* append) {
+                           void* workspace, hipStream_t st, const fsa::AppendArgs* append,
+                           fsa::LaunchFilter* filter = nullptr) {
+  fsa::LaunchFilter all;
+  fsa::LaunchFilter& mk = filter ? *filter : all;
   const SparseWs w = sparse_ws(dims, cfg, max_seq_len);
   // The scoring launch carries the append when no page the append touches can
   // be a candidate: the touched pages start at or after 16 floor(L0 / 16) and
   // candidates end before L0 + n_new - window, so window >= n_new + 15 suffices.
   const bool fused = append && !w.all_taken && cfg.window_tokens >= append->n_new + fsa::kPage - 1;
-  if (append && !fused)
+  if (append && !fused && mk.take())
     FSA_CHECK(hip_status(fsa::launch_append_kv(append->n_new, append->k_new, append->v_new, append->page_table,
                                                append->seq_lens, append->seq_lens_out, append->kc, append->vc,
                                                append->meta, dims->batch, dims->num_kv_heads, dims->head_dim,
@@ -362,7 +365,7 @@ fsa_status run_sparse_step(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_sca
     // every candidate page is selected: the attended set is [0, L), i.e. dense
     // attention; the selection runs only to report the selected pages (it
     // takes all candidates without looking at scores)
-    if (sel_pages)
+    if (sel_pages && mk.take())
       FSA_CHECK(hip_status(fsa::launch_select_pages(at<float>(workspace, w.scores), page_table, seq_lens, sel_pages,
                                                     nullptr, nullptr, dims->batch, dims->num_kv_heads,
                                                     dims->max_pages_per_seq, cfg.prefix_tokens, cfg.window_tokens,
@@ -371,9 +374,10 @@ fsa_status run_sparse_step(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_sca
     const fsa::AttnArgs a = attn_args(dims, n_pages_max(max_seq_len), sm_scale, max_seq_len, q, k_cache, v_cache,
                                       page_table, seq_lens, nullptr, at<float>(workspace, w.part_o),
                                       at<float>(workspace, w.part_ml), out);
-    return hip_status(fsa::launch_attention(fsa::kDense, w.plan, a, st), "dense decode attention launch");
+    return hip_status(fsa::launch_attention(fsa::kDense, w.plan, a, st, &mk), "dense decode attention launch");
   }
-  FSA_CHECK(hip_status(
+  if (mk.take())
+    FSA_CHECK(hip_status(
       fsa::launch_quest_scores(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(meta),
                                fused ? append->seq_lens : seq_lens, at<float>(workspace, w.scores), dims->batch,
                                dims->num_q_heads, dims->num_kv_heads, dims->head_dim,
@@ -410,14 +414,15 @@ fsa_status run_sparse_step(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_sca
   sa.xcd_grouped = w.step.xcd_grouped;
   sa.prefetch = w.step.prefetch;
   sa.scale_log2 = sm_scale * 1.4426950408889634f;
-  FSA_CHECK(hip_status(fsa::launch_select_attend(sa, st), "selection launch"));
+  if (mk.take()) FSA_CHECK(hip_status(fsa::launch_select_attend(sa, st), "selection launch"));
   fsa::AttnArgs a = attn_args(dims, w.step.sel_items, sm_scale, max_seq_len, q, k_cache, v_cache, page_table, seq_lens,
                               at<int32_t>(workspace, w.sel_work), at<float>(workspace, w.part_o),
                               at<float>(workspace, w.part_ml), out);
-  if (w.step.sel_rep > 0) return hip_status(fsa::launch_combine(a, w.slots, st), "combine launch");
+  if (w.step.sel_rep > 0)
+    return mk.take() ? hip_status(fsa::launch_combine(a, w.slots, st), "combine launch") : FSA_OK;
   a.slots_per_unit = w.slots;
   a.slot_base = w.step.pw.wg_per_unit;
-  return hip_status(fsa::launch_attention(fsa::kList, w.plan, a, st), "decode attention launch");
+  return hip_status(fsa::launch_attention(fsa::kList, w.plan, a, st, &mk), "decode attention launch");
 }
 
 // ---------------------------------------------------------------- allocation-free step
@@ -497,6 +502,32 @@ fsa_status fsa_append_decode_attn(const fsa_dims* dims, int32_t n_new, const voi
       dims->num_kv_heads, dims->max_pages_per_seq);
   return run_sparse_step(dims, cfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table, seq_lens_out,
                          out, sel_pages, workspace, static_cast<hipStream_t>(stream), &a);
+}
+
+int32_t fsa_sparse_decode_attn_launches(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_scale,
+                                        int32_t max_seq_len, const void* q, const void* k_cache, const void* v_cache,
+                                        const void* meta, const int32_t* page_table, const int32_t* seq_lens,
+                                        void* out, int32_t* sel_pages, void* workspace, size_t workspace_bytes,
+                                        int32_t first, int32_t last, void* stream) {
+  if (check_step(dims, cfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table, seq_lens, out, workspace,
+                 workspace_bytes) != FSA_OK)
+    return -1;
+  fsa::LaunchFilter count;  // how many launches the step has (none is enqueued)
+  count.first = 1 << 30;
+  if (run_sparse_step(dims, cfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table, seq_lens, out,
+                      sel_pages, workspace, static_cast<hipStream_t>(stream), nullptr, &count) != FSA_OK)
+    return -1;
+  if (first < 0 || last < first || last >= count.count) {
+    fail(FSA_ERR_INVALID_ARG, "launches [%d, %d]: this step has %d launches", first, last, count.count);
+    return -1;
+  }
+  fsa::LaunchFilter some;
+  some.first = first;
+  some.last = last;
+  if (run_sparse_step(dims, cfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table, seq_lens, out,
+                      sel_pages, workspace, static_cast<hipStream_t>(stream), nullptr, &some) != FSA_OK)
+    return -1;
+  return count.count;
 }
 
 int32_t fsa_describe_step(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len, int32_t* info,

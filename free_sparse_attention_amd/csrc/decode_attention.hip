@@ -187,18 +187,20 @@ hipError_t launch_combine(const AttnArgs& a, int slots, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_attention(AttnMode mode, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_attention(AttnMode mode, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream,
+                            LaunchFilter* filter) {
   const unsigned units = (unsigned)(a.batch * a.hkv);
   const dim3 grid(units * (unsigned)plan.wg_per_unit);
   const int slots = a.slots_per_unit > 0 ? a.slots_per_unit : plan.wg_per_unit;
   const int base = a.slots_per_unit > 0 ? a.slot_base : 0;
 #define FSA_ATTN(DD, MM)                                                                                  \
   do {                                                                                                    \
-    hipLaunchKernelGGL((decode_attention_kernel<DD, MM>), grid, dim3(256), 0, stream, a.q, a.kc, a.vc,   \
-                       a.page_table, a.seq_lens, a.work, a.part_o, a.part_ml, a.out, a.hq, a.hkv,         \
-                       a.max_pages, a.max_items, plan.items_per_wave, plan.wg_per_unit, slots, base,      \
-                       a.scale_log2, a.max_seq_len);                                                       \
-    if (slots > 1)                                                                                        \
+    if (!filter || filter->take())                                                                        \
+      hipLaunchKernelGGL((decode_attention_kernel<DD, MM>), grid, dim3(256), 0, stream, a.q, a.kc, a.vc, \
+                         a.page_table, a.seq_lens, a.work, a.part_o, a.part_ml, a.out, a.hq, a.hkv,       \
+                         a.max_pages, a.max_items, plan.items_per_wave, plan.wg_per_unit, slots, base,    \
+                         a.scale_log2, a.max_seq_len);                                                     \
+    if (slots > 1 && (!filter || filter->take()))                                                         \
       hipLaunchKernelGGL((combine_kernel<DD, MM>), dim3((unsigned)(a.batch * a.hq)), dim3(256), 0, stream, \
                          a.part_o, a.part_ml, a.seq_lens, a.out, a.hq, a.hkv,                             \
                          kAttnWaves * plan.items_per_wave, slots, a.max_seq_len);                         \

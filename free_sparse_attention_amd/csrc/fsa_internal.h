@@ -115,6 +115,18 @@ int resident_blocks_per_cu(const void* kernel, int block_threads);
 // ---------------------------------------------------------------- launchers
 // All launchers enqueue on `stream` and return the launch status.
 
+// Launch selection of a decode step (measurement only): `count` numbers the
+// step's launches in order, and take() lets through launches [first, last]
+// (by default all), so a part of the step can be timed on its own.
+struct LaunchFilter {
+  int first = 0, last = 1 << 30;
+  int count = 0;
+  bool take() {
+    const int i = count++;
+    return i >= first && i <= last;
+  }
+};
+
 hipError_t launch_import_kv_plain(const uint16_t* k_plain, const uint16_t* v_plain, uint16_t* kc,
                                   uint16_t* vc, int pool, int hkv, int d, hipStream_t stream);
 
@@ -233,7 +245,8 @@ AttnPlan plan_attention(int units, int max_items);
 
 // Split-K attention over the unit's items, then (when a unit can need more
 // than one workgroup) the combine of its partials.
-hipError_t launch_attention(AttnMode mode, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attention(AttnMode mode, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream,
+                            LaunchFilter* filter = nullptr);
 
 // Merge of all `slots` partials of every unit into the output (decode step).
 hipError_t launch_combine(const AttnArgs& a, int slots, hipStream_t stream);

@@ -31,6 +31,24 @@ int32_t fsa_device_memory(int32_t* info, int32_t n_info);
  * arguments. */
 fsa_status fsa_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
+/* Some of the launches of the fsa_sparse_decode_attn step, so that parts of
+ * the step can be timed: runs only launches first..last (0-based, inclusive)
+ * of the step these arguments describe.  The launches, in order: dense plan
+ * -- [selection, when sel_pages is given], split-K attention, [combine]; wide
+ * plan -- scoring, selection launch (selection replicas + prefix/window
+ * attention), combine; narrow plan -- scoring, selection launch, split-K
+ * attention, combine (fsa_describe_step names the plan).  A launch reads what
+ * the earlier ones left in the workspace, so when first > 0 a whole step with
+ * the same arguments and workspace must have run before on the stream.
+ * Returns the number of launches of the step, or -1 with fsa_last_error() set
+ * (the checks of fsa_sparse_decode_attn, a range outside [0, launches), a
+ * failed launch). */
+int32_t fsa_sparse_decode_attn_launches(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_scale,
+                                        int32_t max_seq_len, const void* q, const void* k_cache, const void* v_cache,
+                                        const void* meta, const int32_t* page_table, const int32_t* seq_lens,
+                                        void* out, int32_t* sel_pages, void* workspace, size_t workspace_bytes,
+                                        int32_t first, int32_t last, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

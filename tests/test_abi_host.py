@@ -213,3 +213,19 @@ def test_noalloc_step_checks_size_before_any_device_call(lib):
         n = (L + 15) // 16
         assert fsa.sparse_decode_workspace_bytes(fsa.dims(B, hq, hkv, 128, n, B * n), fsa.cfg(*cfg), L) <= \
             fsa.NOALLOC_SCRATCH_BYTES
+
+
+def test_launch_range_call_checks_its_arguments(lib):
+    """The measurement call that runs some launches of a step rejects a range
+    outside the step's launches, and the step's own bad arguments, before any launch."""
+    d = _d()
+    c = fsa.cfg(64, 256, 32)
+    p = ctypes.c_void_p(256)  # never dereferenced
+    need = fsa.sparse_decode_workspace_bytes(d, c, 4096)
+    for first, last in ((-1, 0), (0, 3), (2, 1), (3, 3)):  # 4096 tokens, 64 / 256 / 32: the wide plan, 3 launches
+        assert lib.fsa_sparse_decode_attn_launches(ctypes.byref(d), c, 0.1, 4096, p, p, p, p, p, p, p, None, p, need,
+                                                   first, last, None) == -1
+        assert b"launches" in lib.fsa_last_error()
+    assert lib.fsa_sparse_decode_attn_launches(ctypes.byref(d), c, 0.1, 4096, p, p, p, p, p, p, p, None, p, need - 1,
+                                               0, 0, None) == -1
+    assert b"workspace" in lib.fsa_last_error()
