@@ -19,14 +19,18 @@
 //      LDS bins, double-buffered so a pass costs two barriers); one wave scans
 //      the bins for the digit holding the k-th key, and the search stops once
 //      that digit's bin holds exactly the number of keys still needed;
-//   3. per-wave ballots of "taken" form page-ordered 64-bit words (page
-//      t + 1024 j is bit t % 64 of word 16 j + t / 64); every wave scans the
-//      words' popcounts itself, so the output slot of a taken page is a word
-//      prefix plus a popcount within its word: pages come out ascending with
-//      no further barrier.  Only when equal keys straddle the threshold is a
-//      first such scan spent on ranking the tied pages (the lower page id
-//      wins).  Prefix and window items, whose places depend only on the
-//      length and the budget, are written last.
+//   3. the taken pages go to the attention (a replica's slice, or the list
+//      the split-K launch reads) in (wave, lane, column) order: a lane's
+//      own taken count, one wave scan and one barrier place them.  Only when
+//      equal keys straddle the threshold is a first barrier and word scan
+//      spent on ranking the tied pages (the lower page id wins);
+//   4. outputs that must list pages in ascending order (the selected pages,
+//      the stand-alone work list) use per-wave ballots of "taken" as
+//      page-ordered 64-bit words (page t + 1024 j is bit t % 64 of word
+//      16 j + t / 64); every wave scans the words' popcounts itself, so the
+//      slot of a taken page is a word prefix plus a popcount within its word.
+//      Prefix and window items, whose places depend only on the length and
+//      the budget, are written last.
 // The attended set is the disjoint union of three token ranges -- prefix
 // [0, Pe), the middle tokens [Pe, Ws) of selected pages and the window
 // [max(Ws, Pe), L) -- so no token appears twice and no sort or dedup pass is
@@ -52,6 +56,7 @@ struct SelectLds {
   uint32_t hist[2][kSelBins + kWave];  // bins, then one discard slot per lane
   __attribute__((aligned(16))) uint32_t cnt[2][kSelCols * kSelWaves];  // per-word popcounts
   uint32_t mm[2 * kSelWaves];
+  uint32_t wtot[kSelWaves];  // taken pages per wave (items in wave order)
   uint32_t s_prefix, s_need, s_done;
 };
 
@@ -74,9 +79,8 @@ struct SelectJob {  // every optional field defaults to null / zero
   int32_t* counts = nullptr;  // the unit's (k, items), or null
   int32_t* sel_work = nullptr;  // or null: the selected items alone, (page, pool page, lo, hi) at [o],
   int sel_items = 0;            // padded with empty items up to sel_items
-  int4* slice = nullptr;        // or null: selected items [slice_lo, slice_lo + slice_cap) go to
-  int slice_lo = 0, slice_cap = 0;  // slice[o - slice_lo] (typically LDS); with a slice, sel gets only
-                                    // those slots (and its padding only when slice_lo == 0)
+  int4* slice = nullptr;        // or null: selected items [slice_lo, slice_lo + slice_cap), in the
+  int slice_lo = 0, slice_cap = 0;  // attention's item order, go to slice[o - slice_lo] (typically LDS)
   // or null: after the first radix pass, pull into L2 the K and V blocks of
   // some pages already known to be taken (this workgroup's share of them)
   const uint16_t* pf_kc = nullptr;
@@ -295,7 +299,7 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
     }
   }
 
-  // ---- 3. taken pages -> output slots in page order
+  // ---- 3. taken pages: bit j of `mine` marks page tid + 1024 j
   constexpr int nwords = COLS * kSelWaves;
   uint32_t tie_take = 0;  // bit j: this lane's tied page of column j is taken
   if (radix && !done) {
@@ -317,8 +321,8 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
       tie_take |= (uint32_t)(tied && rank < need) << j;
     }
   }
-  // taken pages: bit j of `mine` (one uniform branch, then a lean per-page test)
-  uint32_t mine = 0, wc = 0;
+  // one uniform branch, then a lean per-page test
+  uint32_t mine = 0;
   if (!radix) {
     mine = k == C ? cand : 0u;
   } else if (done) {  // the threshold digit's bin is taken whole
@@ -330,40 +334,73 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
     for (int j = 0; j < COLS; ++j) mine |= (uint32_t)((key[j] >> shift) > kprefix) << j;
     mine = (mine | tie_take) & cand;
   }
-#pragma unroll
-  for (int j = 0; j < COLS; ++j) {
-    const unsigned long long g = __ballot((mine >> j) & 1u);
-    wc = lane == j ? (uint32_t)__popcll(g) : wc;
-  }
-  if (lane < COLS) S.cnt[1][lane * kSelWaves + wave] = wc;
-  __syncthreads();
-  const uint32_t P = wave_word_prefix(S.cnt[1], nwords, wave, lane);
-  int32_t* selw = J.sel_work ? J.sel_work : (J.work ? J.work + 4 * n_pre : nullptr);  // item o of the selection
-  // Slots this call emits: with a slice only the slice's (its share of the
-  // selected pages and of sel), else all.  A column whose slots in this wave
-  // miss that range is skipped with one uniform test.
-  const int e_lo = J.slice ? J.slice_lo : 0;
+
+  // ---- 4. items for the attention (a slice of them, or the selected-item
+  // list of the split-K launch) in (wave, lane, column) order.  Any fixed
+  // order serves the attention, and this one needs only the lane's own
+  // taken count, one wave scan and one barrier: item o of lane l of wave w
+  // is its i-th taken page, o = (taken pages of waves < w) + (of lanes < l
+  // in w) + i.  Page order (step 5) costs a ballot per column.
+  const int e_lo = J.slice ? J.slice_lo : 0;  // items this call emits: the slice's, or all
   const int e_hi = J.slice ? J.slice_lo + J.slice_cap : 0x7FFFFFFF;
-#pragma unroll
-  for (int j = 0; j < COLS; ++j) {
-    const bool t = (mine >> j) & 1u;
-    const unsigned long long g = __ballot(t);
-    // read the word prefix with every lane active: a lane read inside the
-    // branch below may be inactive and hold no defined value
-    const int base = __builtin_amdgcn_readlane((int)P, 2 * j + (wave >> 3));
-    if (base < e_hi && base + (int)__popcll(g) > e_lo && t) {
-      const int p = tid + kSelThreads * j;
-      const int o = base + (int)lanes_below(g);
+  if (J.slice || J.sel_work) {
+    const uint32_t cnt = (uint32_t)__popc(mine);
+    const uint32_t incl = wave_incl_sum(cnt);
+    if (lane == kWave - 1) S.wtot[wave] = incl;
+    __syncthreads();
+    const uint32_t wt = lane < kSelWaves ? S.wtot[lane] : 0u;
+    const int base = __builtin_amdgcn_readlane((int)(wave_incl_sum(wt) - wt), wave);
+    int o = base + (int)(incl - cnt);
+    uint32_t m = mine;
+    while (m) {
+      const int j = __builtin_ctz(m);
+      m &= m - 1;
       if (o >= e_lo && o < e_hi) {
-        if (J.sel) J.sel[o] = p;
+        const int p = tid + kSelThreads * j;
         const int lo = max(p * kPage, Pe) - p * kPage, hi = min(p * kPage + kPage, Ws) - p * kPage;
-        if (selw) put_item(selw, o, p, S.sphys[p], lo, hi);
-        if (J.slice) J.slice[o - e_lo] = make_int4(p, S.sphys[p], lo, hi);
+        const int phys = S.sphys[p];
+        if (J.slice) J.slice[o - e_lo] = make_int4(p, phys, lo, hi);
+        if (J.sel_work) put_item(J.sel_work, o, p, phys, lo, hi);
+      }
+      ++o;
+    }
+  }
+
+  // ---- 5. outputs in page order (the selected pages, the stand-alone work
+  // list): per-wave ballot words in page order, every wave scanning the
+  // words' popcounts itself, so the slot of a taken page is a word prefix
+  // plus a popcount within its word
+  if (J.sel || J.work) {
+    uint32_t wc = 0;
+#pragma unroll
+    for (int j = 0; j < COLS; ++j) {
+      const unsigned long long g = __ballot((mine >> j) & 1u);
+      wc = lane == j ? (uint32_t)__popcll(g) : wc;
+    }
+    if (lane < COLS) S.cnt[1][lane * kSelWaves + wave] = wc;
+    __syncthreads();
+    const uint32_t P = wave_word_prefix(S.cnt[1], nwords, wave, lane);
+    int32_t* selw = J.work ? J.work + 4 * n_pre : nullptr;  // item o of the selection
+#pragma unroll
+    for (int j = 0; j < COLS; ++j) {
+      const bool t = (mine >> j) & 1u;
+      const unsigned long long g = __ballot(t);
+      // read the word prefix with every lane active: a lane read inside the
+      // branch below may be inactive and hold no defined value
+      const int base = __builtin_amdgcn_readlane((int)P, 2 * j + (wave >> 3));
+      if (t) {
+        const int p = tid + kSelThreads * j;
+        const int o = base + (int)lanes_below(g);
+        if (J.sel) J.sel[o] = p;
+        if (selw) {
+          const int lo = max(p * kPage, Pe) - p * kPage, hi = min(p * kPage + kPage, Ws) - p * kPage;
+          put_item(selw, o, p, S.sphys[p], lo, hi);
+        }
       }
     }
   }
   // Stores come last: on this target every load wait also waits for earlier stores.
-  if (J.sel && e_lo == 0)  // the padding, by the call whose slots start at 0
+  if (J.sel)
     for (int i = k + tid; i < J.budget; i += kSelThreads) J.sel[i] = -1;
   if (tid == 0 && J.counts) {
     J.counts[0] = k;

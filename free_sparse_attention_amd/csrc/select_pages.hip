@@ -128,8 +128,8 @@ __device__ __forceinline__ SelectJob step_job(const StepArgs& A, int unit) {
 
 // Wide plan, selection role: the sel_rep workgroups of a unit each run the
 // unit's selection (deterministic, so the replicas agree) and then attend
-// their own slice of the selected pages, in output-slot order: replica r takes
-// selected items [r per, (r + 1) per), at most two per wave.  Running the
+// their own slice of the selected pages, in the selection's item order:
+// replica r takes selected items [r per, (r + 1) per), at most two per wave.  Running the
 // selection redundantly on otherwise idle CUs costs nothing on the critical
 // path and spares a launch and a round trip for a work list.
 template <int COLS, int D>
@@ -146,6 +146,7 @@ __device__ __forceinline__ void select_and_attend(SelectLds& SL, MergeLds<D, kSe
   J.slice = slice;
   J.slice_lo = r * A.per;
   J.slice_cap = A.per;
+  if (r != 0) J.sel = nullptr;  // the selected pages, when asked for, are written by replica 0
   if (kCanPrefetch && A.prefetch) {  // the unit's replicas share an L2: each warms its share of the taken pages
     J.pf_kc = A.kc;
     J.pf_vc = A.vc;
