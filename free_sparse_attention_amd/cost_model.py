@@ -17,11 +17,10 @@ Terms, per step (sums over the B x Hkv (sequence, KV head) units):
 * otherwise the step runs the dense kernels: the dense cost;
 * dense: ``d0 + d_kv * K/V MB``.
 
-The plan terms follow the library's launch planning: every candidate taken
-when C(L) <= budget; the wide plan when selection replicas with one (else
-two) selected pages per wave fit on half the CUs; else the narrow plan with
-a separate split-K launch.  The selection's pages per thread is the power of
-two that covers ceil(L / 16) pages with 1024 threads.
+The plan terms (which plan, pages per selection thread, selected pages per
+replica) are the library's own, read from ``fsa_describe_step``; the fit is
+checked against measured points it was not fitted to
+(``cost_model_holdout.json``, ``bench.py --holdout``).
 """
 from __future__ import annotations
 
@@ -33,6 +32,7 @@ import numpy as np
 
 PAGE = 16
 _DATA = os.path.join(os.path.dirname(os.path.abspath(__file__)), "cost_model_data.json")
+_HOLDOUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "cost_model_holdout.json")
 
 
 @dataclass(frozen=True)
@@ -48,28 +48,29 @@ class StepShape:
 
 
 def _features(s: StepShape, compute_units: int) -> dict:
+    """Byte counts of the step, and its launch plan as the library itself
+    plans it (fsa_describe_step: host only; without a device the library
+    plans for MI355X's 256 compute units)."""
+    from . import _lib
+
     units = s.batch * s.kv_heads
     n = -(-s.seq_len // PAGE)
     pe, ws = min(s.prefix, s.seq_len), max(0, s.seq_len - s.window)
     cand = (-(-ws // PAGE) - pe // PAGE) if pe < ws else 0
     k = min(s.budget_pages, cand)
-    sel_items = max(1, min(s.budget_pages, n))
-    ipw_sel, narrow = 0, 1
-    for ipw in (1, 2):
-        rep = -(-sel_items // (16 * ipw))
-        if units * rep <= compute_units // 2:
-            ipw_sel, narrow = ipw, 0
-            break
-    cols = 1
-    while cols * 1024 < n:
-        cols *= 2
+    d = _lib.dims(s.batch, s.q_heads, s.kv_heads, s.head_dim, n, s.batch * n)
+    plan = _lib.describe_step(d, _lib.cfg(s.prefix, s.window, s.budget_pages), s.seq_len)
+    wide = plan["plan"] == "wide"
     page_kv = 2 * PAGE * s.head_dim * 2  # K and V bytes of one page of one KV head
     return {
-        "all_taken": cand <= s.budget_pages,
+        "all_taken": plan["plan"] == "dense",
         "meta_mb": units * cand * 4 * s.head_dim / 1e6,
         "sel_mb": units * k * page_kv / 1e6,
         "dense_mb": units * n * page_kv / 1e6,
-        "cols": cols, "ipw": ipw_sel, "narrow": narrow,
+        "cols": plan["select_cols"],
+        # selected pages each wave of a selection replica attends (wide plan)
+        "ipw": -(-plan["per_replica"] // 16) if wide else 0,
+        "narrow": int(plan["plan"] == "narrow"),
     }
 
 
