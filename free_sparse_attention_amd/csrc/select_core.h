@@ -15,8 +15,10 @@
 //      instructions as possible;
 //   2. the k-th largest candidate key is found exactly by most-significant-
 //      digit radix select: digits start right below the bits that the
-//      smallest and the largest candidate key share, 11 bits at a time (2048
-//      LDS bins, double-buffered so a pass costs two barriers); one wave scans
+//      smallest and the largest candidate key share, 10 bits at a time (1024
+//      LDS bins, double-buffered so a pass costs two barriers; 10-bit digits
+//      conflict less in the LDS atomics than 11-bit ones and still resolve
+//      the threshold in two passes at 64k-256k tokens); one wave scans
 //      the bins for the digit holding the k-th key, and the search stops once
 //      that digit's bin holds exactly the number of keys still needed;
 //   3. the taken pages go to the attention (a replica's slice, or the list
@@ -45,8 +47,9 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kSelCols = 32;  // pages per thread: up to 32768 (512k tokens)
 constexpr int kSelMaxPages = kSelThreads * kSelCols;
-constexpr int kSelDigitBits = 11;
+constexpr int kSelDigitBits = 10;
 constexpr int kSelBins = 1 << kSelDigitBits;
+static_assert(kSelBins / kWave % 8 == 0, "the bin scan sums each lane's bins in pairs of 16-byte reads");
 
 // s_waitcnt immediate for vmcnt(0) with the other counters left alone
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -259,7 +262,7 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
         for (int i = tid; i < kSelBins; i += kSelThreads) h_next[i] = 0;  // for the next pass
         __syncthreads();
         if (wave == 0) {
-          // lane l owns digits 2047 - 32 l ... 2016 - 32 l (largest first)
+          // lane l owns the PER_LANE digits below kSelBins - PER_LANE l (largest first)
           constexpr int PER_LANE = kSelBins / kWave;
           const uint4* hv = reinterpret_cast<const uint4*>(h + kSelBins - PER_LANE * (lane + 1));
           uint32_t part[PER_LANE / 4];
@@ -274,7 +277,7 @@ __device__ __forceinline__ SelectResult select_unit(SelectLds& S, const SelectJo
           const uint32_t incl = wave_incl_sum(s);
           const int f = __ffsll((long long)__ballot(incl >= need)) - 1;  // first lane reaching `need`
           const uint32_t before = (uint32_t)__builtin_amdgcn_readlane((int)(incl - s), f);
-          // the wave scans lane f's 32 digits (lanes 32..63 carry zeros)
+          // the wave scans lane f's PER_LANE digits (the lanes from PER_LANE on carry zeros)
           const uint32_t digit = (uint32_t)(kSelBins - 1 - PER_LANE * f - (lane & (PER_LANE - 1)));
           const uint32_t c = (lane < PER_LANE) ? h[digit] : 0u;
           const uint32_t ic = wave_incl_sum(c);
