@@ -54,13 +54,16 @@ __device__ __forceinline__ void load_q_operand(const uint16_t* q_group, int G, b
 // One wave attends its first n items; lane j holds item j's pool page and
 // token range.  n must be wave-uniform.  PIPE: two-stage pipeline (the next
 // page's loads in flight while the current page is computed); otherwise one
-// page at a time with fewer registers.  head_off/page_stride locate KV head g
-// of a pool page in both caches.
-template <int D, bool PIPE>
+// page at a time with fewer registers.  QLDS (with PIPE): n <= 2, both pages'
+// loads in flight together, and the query operand read from LDS
+// (q_lds[ks * 64 + lane], the layout of qb) to leave the registers to the
+// second page.  head_off/page_stride locate KV head g of a pool page in both
+// caches.
+template <int D, bool PIPE, bool QLDS = false>
 __device__ __forceinline__ void attend_items(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
                                              size_t head_off, size_t page_stride, const bf16x8_t (&qb)[D / 32],
                                              int my_phys, int my_lo, int my_hi, int n, float scale_log2,
-                                             WaveAttn<D>& st) {
+                                             WaveAttn<D>& st, const bf16x8_t* q_lds = nullptr) {
   constexpr int NKS = D / 32;  // QK k-steps
   constexpr int NDT = D / 16;  // PV d-tiles
   const int lane = threadIdx.x & 63, col = lane & 15, gq = lane >> 4;
@@ -83,7 +86,8 @@ __device__ __forceinline__ void attend_items(const uint16_t* __restrict__ kc, co
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[ks]), qb[ks], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[ks]),
+                                                  QLDS ? q_lds[ks * kWave + lane] : qb[ks], s, 0, 0, 0);
     float x[4], mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -117,7 +121,22 @@ __device__ __forceinline__ void attend_items(const uint16_t* __restrict__ kc, co
     }
   };
 
-  if (PIPE) {
+  if (PIPE && QLDS) {
+    // at most two items: both pages' loads in flight together, the second
+    // issued even for one item (page 0 again, then attended as an empty
+    // range, which leaves the state unchanged) so that no branch separates
+    // the loads from the computation
+    if (n > 0) {
+      uint4 kA[NKS], kB[NKS];
+      uint2 vA[NDT], vB[NDT];
+      load(0, kA, vA);
+      __builtin_amdgcn_sched_barrier(0);  // issue order = completion order: the first page's wait leaves the second in flight
+      load(n > 1 ? 1 : 0, kB, vB);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(0, kA, vA);
+      compute(1, kB, vB);
+    }
+  } else if (PIPE) {
     // Every trip of the loop issues exactly one page of loads and consumes
     // one, so the number of loads in flight at the loop head is the same on
     // entry and on the back edge and the compiler waits only for the page

@@ -131,10 +131,15 @@ __device__ __forceinline__ SelectJob step_job(const StepArgs& A, int unit) {
 // their own slice of the selected pages, in the selection's item order:
 // replica r takes selected items [r per, (r + 1) per), at most two per wave.  Running the
 // selection redundantly on otherwise idle CUs costs nothing on the critical
-// path and spares a launch and a round trip for a work list.
+// path and spares a launch and a round trip for a work list.  Up to 8 pages
+// per thread the query operand is loaded into registers with the selection's
+// first loads and a wave attends one page at a time (the registers left
+// beside the prefetch words); from 16 pages per thread, where each wave may
+// have two pages, the first D/32 waves copy the operand straight into LDS with
+// the selection's first loads and both pages are in flight together.
 template <int COLS, int D>
 __device__ __forceinline__ void select_and_attend(SelectLds& SL, MergeLds<D, kSelWaves>& SM, int4* slice,
-                                                  const StepArgs& A, int unit, int r) {
+                                                  bf16x8_t* q_lds, const StepArgs& A, int unit, int r) {
   const int b = unit / A.hkv, g = unit % A.hkv, G = A.hq / A.hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // the query operand is loaded first, so that waiting for it later does not
@@ -142,6 +147,13 @@ __device__ __forceinline__ void select_and_attend(SelectLds& SL, MergeLds<D, kSe
   bf16x8_t qb[D / 32];
   constexpr bool kCanPrefetch = COLS <= 8;  // beyond, the early query operand costs registers
   if (kCanPrefetch) load_q_operand<D>(A.q + ((size_t)b * A.hq + (size_t)g * G) * D, G, qb);
+  if (!kCanPrefetch && wave < D / 32) {  // k-step `wave` of the operand straight to LDS; padding columns
+    // repeat head G - 1 (their results are never written)
+    const int col = lane & 15, gq = lane >> 4;
+    const uint16_t* src = A.q + ((size_t)b * A.hq + (size_t)g * G + min(col, G - 1)) * D + 32 * wave + 8 * gq;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)(q_lds + wave * kWave), 16, 0, 0);
+  }
   SelectJob J = step_job(A, unit);
   J.slice = slice;
   J.slice_lo = r * A.per;
@@ -169,10 +181,13 @@ __device__ __forceinline__ void select_and_attend(SelectLds& SL, MergeLds<D, kSe
   }
   __syncthreads();  // every read of the selection's LDS precedes the merge that reuses it
   const int n = __popcll(__ballot(my_lo < my_hi));  // a prefix of the wave's lanes
-  if (!kCanPrefetch) load_q_operand<D>(A.q + ((size_t)b * A.hq + (size_t)g * G) * D, G, qb);
   WaveAttn<D> st;
-  attend_items<D, false>(A.kc, A.vc, (size_t)g * (kPage * D), (size_t)A.hkv * (kPage * D), qb, my_phys, my_lo,
-                         my_hi, n, A.scale_log2, st);
+  if constexpr (kCanPrefetch)
+    attend_items<D, false>(A.kc, A.vc, (size_t)g * (kPage * D), (size_t)A.hkv * (kPage * D), qb, my_phys, my_lo,
+                           my_hi, n, A.scale_log2, st);
+  else
+    attend_items<D, true, true>(A.kc, A.vc, (size_t)g * (kPage * D), (size_t)A.hkv * (kPage * D), qb, my_phys,
+                                my_lo, my_hi, n, A.scale_log2, st, q_lds);
   // the prefetch words are used here, after the attention's own loads
   asm volatile("" ::"v"(R.pf[0]), "v"(R.pf[1]), "v"(R.pf[2]), "v"(R.pf[3]));
   const size_t slot = (size_t)unit * A.slots_per_unit + A.pw_wg + r;
@@ -193,6 +208,7 @@ __global__ __launch_bounds__(kSelThreads) void select_attend_kernel(const StepAr
     MergeLds<D, kSelWaves> att;
   } U;
   __shared__ int4 slice[kSliceMax];
+  __shared__ bf16x8_t q_lds[D / 32 * kWave];
   const int units = A.batch * A.hkv;
   const int i = blockIdx.x;
   if (i < A.sel_blocks) {
@@ -204,7 +220,7 @@ __global__ __launch_bounds__(kSelThreads) void select_attend_kernel(const StepAr
         r = k % A.sel_rep;
         if (unit >= units) return;
       }
-      select_and_attend<COLS, D>(U.sel, U.att, slice, A, unit, r);
+      select_and_attend<COLS, D>(U.sel, U.att, slice, q_lds, A, unit, r);
     } else {
       // narrow plan: the selected items go to the work list of the split-K
       // attention kernel
@@ -273,9 +289,7 @@ StepPlan plan_step(int units, int head_dim, int prefix, int window, int budget, 
   StepPlan p;
   p.sel_items = std::max(1, std::min(budget, n_max));
   // Wide when the selection replicas fit on half the CUs with one, else two,
-  // selected pages per wave (one page at a time: a two-stage pipeline does not
-  // fit beside the selection in 128 registers); the prefix/window workgroups
-  // take the other CUs.
+  // selected pages per wave; the prefix/window workgroups take the other CUs.
   p.sel_rep = 0;
   p.per = 0;
   for (int ipw = 1; ipw <= 2 && p.sel_rep == 0; ++ipw) {
