@@ -104,19 +104,34 @@ def launch_bytes(wl, plan):
     return [kv_all + pt + q, out]
 
 
+# the sources each kernel is compiled from (a counter record holds their hash)
+KERNEL_SOURCES = {
+    "quest_score_kernel": ["free_sparse_attention_amd/csrc/quest_score.hip",
+                           "free_sparse_attention_amd/csrc/append_core.h",
+                           "free_sparse_attention_amd/csrc/fsa_internal.h"],
+    "select_attend_kernel": ["free_sparse_attention_amd/csrc/select_pages.hip",
+                             "free_sparse_attention_amd/csrc/select_core.h",
+                             "free_sparse_attention_amd/csrc/attend_core.h",
+                             "free_sparse_attention_amd/csrc/fsa_internal.h"]}
+
+
+def sources_sha256(sources) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in sources:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(kernel: str, sources, workload: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter runs
     (profiles/<kernel>_<workload>_counters.json), or None when any of its
     sources has changed since the counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "%s_%s_counters.json" % (kernel, workload))
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    h = hashlib.sha256()
-    for f in sources:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if h.hexdigest() != rec.get("sources_sha256"):
+    if sources_sha256(sources) != rec.get("sources_sha256"):
         return None
     return rec["hbm_bytes_per_launch"]
 
@@ -282,12 +297,38 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
         return run
 
     assert prefix_fn(0)(0) == len(names), (plan, names)
-    pre = [timed(prefix_fn(j), steps, min(warmup, 10)) for j in range(len(names))]
+    # the prefixes are timed in interleaved rounds, so that a slow stretch of
+    # the run does not land on one prefix only
+    rounds = 5
+    pre = [0.0] * len(names)
+    for _ in range(rounds):
+        for j in range(len(names)):
+            pre[j] += timed(prefix_fn(j), max(1, steps // rounds), min(warmup, 10)) / rounds
     per = [pre[0]] + [max(1e-6, pre[j] - pre[j - 1]) for j in range(1, len(names))]
+
+    # cross-check: every launch of `steps` rotated steps bracketed by its own
+    # pair of HIP events on the step's stream (the event markers add about
+    # 1.5-2.5 us to each launch, so this overstates a launch's duration)
+    def bracketed(n, w):
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
+              for _ in range(n)]
+        for i in range(w + n):
+            k, v, m = reps[i % R]
+            for j in range(len(names)):
+                if i >= w:
+                    ev[i - w][j][0].record(stream)
+                fsa.sparse_decode_attn_launches(base.dims, c, wl.sm_scale, msl, base.q, k, v, m, base.page_table,
+                                                base.seq_lens, out, None, ws, j, j, stream)
+                if i >= w:
+                    ev[i - w][j][1].record(stream)
+        torch.cuda.synchronize()
+        return [sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(n)) / n for j in range(len(names))]
+
+    own = bracketed(steps, min(warmup, 10))
     lb = launch_bytes(wl, plan)
     launches = [{"kernel": names[j], "avg_launch_us": 1000.0 * per[j], "alg_bytes": lb[j],
                  "achieved_GBps": lb[j] / (per[j] * 1e-3) / 1e9, "frac": lb[j] / (per[j] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                 "time_share": per[j] / sum(per)} for j in range(len(names))]
+                 "bracketed_us": 1000.0 * own[j], "time_share": per[j] / sum(per)} for j in range(len(names))]
     marked_ms = sum(per)
 
     res = {"ms_per_step": ms_step, "steps_per_s": 1000.0 / ms_step, "step_alg_bytes": step_bytes,
@@ -670,11 +711,7 @@ def main():
 
     r = main_res
     top = max(r["launches"], key=lambda x: x["avg_launch_us"])
-    src = {"quest_score_kernel": ["free_sparse_attention_amd/csrc/quest_score.hip",
-                                  "free_sparse_attention_amd/csrc/append_core.h"],
-           "select_attend_kernel": ["free_sparse_attention_amd/csrc/select_pages.hip",
-                                    "free_sparse_attention_amd/csrc/select_core.h",
-                                    "free_sparse_attention_amd/csrc/attend_core.h"]}.get(top["kernel"])
+    src = KERNEL_SOURCES.get(top["kernel"])
     line = {
         "metric": "sparse decode-attn steps/sec + achieved HBM GB/s (% peak) at 64k/256k ctx",
         "value": r["steps_per_s"], "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
