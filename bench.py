@@ -246,6 +246,9 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n  # ms
 
+    # spread first (20 repetitions of 50 steps), then the step timing proper:
+    # `warmup` untimed steps and `steps` timed ones
+    reps_us = sorted(1000.0 * timed(step, 50, 0) for _ in range(20))
     log(f"[bench] {wl.name}: {warmup} warmup + {steps} timed steps")
     ms_step = timed(step, steps, warmup)
 
@@ -254,9 +257,7 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
         fsa.sparse_decode_attn(base.dims, c, wl.sm_scale, msl, base.q, k, v, m, base.page_table, base.seq_lens,
                                out, None, ws, stream)
 
-    warm_ms = timed(warm_step, steps, warmup)
-    # spread: 20 repetitions of 50 steps
-    reps_us = sorted(1000.0 * timed(step, 50, 0) for _ in range(20))
+    warm_ms = timed(warm_step, max(steps, 100), max(warmup, 10))
     # cold: single steps, each after a 1 GiB scrub that evicts L2 and the Infinity Cache
     scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     cold_us = []
@@ -283,7 +284,7 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
 
     # each launch of the step timed live with HIP events on the step's
     # stream, in its place in the step: the prefix of launches 0..j is timed
-    # over `steps` rotated steps, and launch j is charged the difference
+    # over at least 200 rotated steps, and launch j is charged the difference
     # between prefixes j and j - 1 (so the launches add up to the step)
     plan = fsa.describe_step(base.dims, c, msl)["plan"]
     names = LAUNCHES[plan]
@@ -299,14 +300,14 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
     assert prefix_fn(0)(0) == len(names), (plan, names)
     # the prefixes are timed in interleaved rounds, so that a slow stretch of
     # the run does not land on one prefix only
-    rounds = 5
+    rounds, n_l = 5, max(steps, 200)
     pre = [0.0] * len(names)
     for _ in range(rounds):
         for j in range(len(names)):
-            pre[j] += timed(prefix_fn(j), max(1, steps // rounds), min(warmup, 10)) / rounds
+            pre[j] += timed(prefix_fn(j), n_l // rounds, 10) / rounds
     per = [pre[0]] + [max(1e-6, pre[j] - pre[j - 1]) for j in range(1, len(names))]
 
-    # cross-check: every launch of `steps` rotated steps bracketed by its own
+    # cross-check: every launch of as many rotated steps bracketed by its own
     # pair of HIP events on the step's stream (the event markers add about
     # 1.5-2.5 us to each launch, so this overstates a launch's duration)
     def bracketed(n, w):
@@ -324,7 +325,7 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
         torch.cuda.synchronize()
         return [sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(n)) / n for j in range(len(names))]
 
-    own = bracketed(steps, min(warmup, 10))
+    own = bracketed(n_l, 10)
     lb = launch_bytes(wl, plan)
     launches = [{"kernel": names[j], "avg_launch_us": 1000.0 * per[j], "alg_bytes": lb[j],
                  "achieved_GBps": lb[j] / (per[j] * 1e-3) / 1e9, "frac": lb[j] / (per[j] * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -347,7 +348,7 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
             fsa.dense_decode_attn(base.dims, wl.sm_scale, msl, base.q, k, v, base.page_table, base.seq_lens,
                                   out, dws, stream)
 
-        ms_dense = timed(dense, max(10, steps // 4), 3)
+        ms_dense = timed(dense, max(20, steps // 4), 3)
         res["dense_ms_per_step"] = ms_dense
         res["speedup_vs_dense"] = ms_dense / ms_step
     # copy-kernel probe of known size (reference for the rocprofv3 byte counters)
