@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     meta_bytes,
     quest_scores,
     read_probe,
+    build_flags,
     select_pages,
     sparse_decode_attn,
     sparse_decode_attn_noalloc,

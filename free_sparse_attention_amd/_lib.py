@@ -7,6 +7,7 @@ or a call fails, an exception is raised.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -15,6 +16,8 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfsa.so")
+# debug build whose kernels poison their LDS (see build.py); tests only
+POISON_LIB_PATH = os.path.join(_PKG, "libfsa_poison.so")
 
 FSA_OK, FSA_ERR_INVALID_ARG, FSA_ERR_UNSUPPORTED, FSA_ERR_WORKSPACE, FSA_ERR_HIP = range(5)
 
@@ -24,7 +27,7 @@ EXPORTED = (
     "fsa_sparse_decode_workspace_bytes", "fsa_sparse_decode_attn",
     "fsa_dense_decode_workspace_bytes", "fsa_dense_decode_attn", "fsa_validate_inputs", "fsa_describe_step",
     "fsa_append_decode_attn", "fsa_device_memory", "fsa_read_probe", "fsa_sparse_decode_attn_noalloc",
-    "fsa_sparse_decode_attn_launches",
+    "fsa_sparse_decode_attn_launches", "fsa_build_flags",
 )
 
 
@@ -48,48 +51,72 @@ class LayerCfg(ctypes.Structure):
 
 _lock = threading.Lock()
 _lib = None
+_opened = {}
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libfsa.so and declare its signatures (raises if it is not built)."""
+    """Load libfsa.so and declare its signatures (raises if it is not built).
+    Later calls return the library in use (see ``using``)."""
     global _lib
     with _lock:
-        if _lib is not None:
-            return _lib
-        if not os.path.exists(path):
-            raise RuntimeError(f"{path} is not built; run `python -m free_sparse_attention_amd.build`")
-        L = ctypes.CDLL(path)
-        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
-        D, C = ctypes.POINTER(Dims), LayerCfg
-        sig = {
-            "fsa_last_error": (ctypes.c_char_p, []),
-            "fsa_import_kv_plain": (i32, [D, vp, vp, vp, vp, vp]),
-            "fsa_append_kv": (i32, [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
-            "fsa_build_page_meta": (i32, [D, vp, vp, vp, vp, vp]),
-            "fsa_meta_bytes": (sz, [D]),
-            "fsa_quest_scores": (i32, [D, C, i32, vp, vp, vp, vp, vp]),
-            "fsa_max_work_items": (i32, [D, C, i32]),
-            "fsa_select_pages": (i32, [D, C, i32, vp, vp, vp, vp, vp, vp, vp]),
-            "fsa_sparse_decode_workspace_bytes": (sz, [D, C, i32]),
-            "fsa_sparse_decode_attn": (i32, [D, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
-            "fsa_sparse_decode_attn_noalloc": (i32, [D, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
-            "fsa_sparse_decode_attn_launches": (i32, [D, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, i32,
-                                                      vp]),
-            "fsa_dense_decode_workspace_bytes": (sz, [D, i32]),
-            "fsa_dense_decode_attn": (i32, [D, f32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
-            "fsa_validate_inputs": (i32, [D, i32, i32, vp, vp, vp, vp, vp]),
-            "fsa_describe_step": (i32, [D, C, i32, ctypes.POINTER(i32), i32]),
-            "fsa_append_decode_attn": (i32, [D, i32, vp, vp, vp, vp, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
-                                             sz, vp]),
-            "fsa_device_memory": (i32, [ctypes.POINTER(i32), i32]),
-            "fsa_read_probe": (i32, [vp, sz, vp, vp]),
-        }
-        for name, (res, args) in sig.items():
-            f = getattr(L, name)
-            f.restype = res
-            f.argtypes = args
-        _lib = L
-        return L
+        if _lib is None:
+            _lib = _open(path)
+        return _lib
+
+
+@contextlib.contextmanager
+def using(path: str):
+    """Run the binding's calls on another build of the library (same ABI), e.g.
+    the LDS-poison debug build, inside the ``with`` block."""
+    global _lib
+    load()
+    with _lock:
+        prev, _lib = _lib, _open(path)
+    try:
+        yield _lib
+    finally:
+        with _lock:
+            _lib = prev
+
+
+def _open(path: str) -> ctypes.CDLL:
+    if path in _opened:
+        return _opened[path]
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m free_sparse_attention_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    D, C = ctypes.POINTER(Dims), LayerCfg
+    sig = {
+        "fsa_last_error": (ctypes.c_char_p, []),
+        "fsa_import_kv_plain": (i32, [D, vp, vp, vp, vp, vp]),
+        "fsa_append_kv": (i32, [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "fsa_build_page_meta": (i32, [D, vp, vp, vp, vp, vp]),
+        "fsa_meta_bytes": (sz, [D]),
+        "fsa_quest_scores": (i32, [D, C, i32, vp, vp, vp, vp, vp]),
+        "fsa_max_work_items": (i32, [D, C, i32]),
+        "fsa_select_pages": (i32, [D, C, i32, vp, vp, vp, vp, vp, vp, vp]),
+        "fsa_sparse_decode_workspace_bytes": (sz, [D, C, i32]),
+        "fsa_sparse_decode_attn": (i32, [D, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "fsa_sparse_decode_attn_noalloc": (i32, [D, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "fsa_sparse_decode_attn_launches": (i32, [D, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, i32,
+                                                  vp]),
+        "fsa_dense_decode_workspace_bytes": (sz, [D, i32]),
+        "fsa_dense_decode_attn": (i32, [D, f32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "fsa_validate_inputs": (i32, [D, i32, i32, vp, vp, vp, vp, vp]),
+        "fsa_describe_step": (i32, [D, C, i32, ctypes.POINTER(i32), i32]),
+        "fsa_append_decode_attn": (i32, [D, i32, vp, vp, vp, vp, C, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         sz, vp]),
+        "fsa_device_memory": (i32, [ctypes.POINTER(i32), i32]),
+        "fsa_read_probe": (i32, [vp, sz, vp, vp]),
+        "fsa_build_flags": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _opened[path] = L
+    return L
 
 
 def _check(status: int) -> None:
@@ -184,6 +211,11 @@ def device_memory() -> dict:
     if n < 0:
         raise FsaError(FSA_ERR_HIP, load().fsa_last_error().decode())
     return {k: int(buf[i]) for i, k in enumerate(MEMORY_INFO[:n])}
+
+
+def build_flags() -> int:
+    """fsa_build_flags of the library in use: bit 0 = LDS-poison debug build."""
+    return int(load().fsa_build_flags())
 
 
 def read_probe(buf, sink, stream=None):

@@ -1,4 +1,4 @@
-"""Build libfsa.so (gfx950) in-tree with hipcc.
+"""Build libfsa.so (gfx950) in-tree with hipcc, and its LDS-poison debug twin.
 
     python -m free_sparse_attention_amd.build
 """
@@ -11,6 +11,9 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libfsa.so")
+# Debug build: every kernel fills its LDS with a NaN pattern at the start and
+# between stages that reuse it (-DFSA_DEBUG_POISON_LDS); tests only.
+POISON_LIB = os.path.join(PKG, "libfsa_poison.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -27,16 +30,25 @@ def sources() -> list[str]:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libfsa.so (always recompiles)."""
+    """Compile every HIP source into libfsa.so and, in parallel, into
+    libfsa_poison.so (always recompiles both).  Returns the release library."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, *sources()]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    jobs = []
+    for out, extra in ((LIB, []), (POISON_LIB, ["-DFSA_DEBUG_POISON_LDS"])):
+        tmp = out + f".tmp{os.getpid()}"
+        cmd = [hipcc, *HIPCC_FLAGS, *extra, "-o", tmp, *sources()]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((out, tmp, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    failed = []
+    for out, tmp, p in jobs:
+        so, se = p.communicate()
+        if p.returncode != 0:
+            failed.append(f"{os.path.basename(out)}: hipcc failed ({p.returncode}):\n{so}\n{se}")
+        else:
+            os.replace(tmp, out)
+    if failed:
+        raise RuntimeError("\n".join(failed))
     return LIB
 
 

@@ -552,6 +552,8 @@ int32_t fsa_describe_step(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_s
   return n;
 }
 
+int32_t fsa_build_flags(void) { return fsa::kBuildFlags; }
+
 int32_t fsa_device_memory(int32_t* info, int32_t n_info) {
   if (!info || n_info < 0) {
     fail(FSA_ERR_INVALID_ARG, "info must be non-null and n_info >= 0");

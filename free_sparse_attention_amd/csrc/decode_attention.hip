@@ -32,6 +32,7 @@ __global__ __launch_bounds__(256, 3) void decode_attention_kernel(
     uint16_t* __restrict__ out, int hq, int hkv, int max_pages, int max_items, int ipw,
     int wg_per_unit, int slots_per_unit, int slot_base, float scale_log2, int max_seq_len) {
   __shared__ MergeLds<D, kAttnWaves> S;
+  poison_lds(&S, sizeof(S));
 
   const int unit = blockIdx.x / wg_per_unit, wg = blockIdx.x % wg_per_unit;
   const int b = unit / hkv, g = unit % hkv, G = hq / hkv;
@@ -93,6 +94,9 @@ __global__ __launch_bounds__(256) void combine_kernel(
   constexpr int PARTS = 256 / NQ;  // threads sharing a column, each with every PARTS-th partial
   __shared__ float sh_m[PARTS][NQ], sh_l[PARTS][NQ];
   __shared__ float4 sh_acc[PARTS][NQ];
+  poison_lds(sh_m, sizeof(sh_m));
+  poison_lds(sh_l, sizeof(sh_l));
+  poison_lds(sh_acc, sizeof(sh_acc));
   const int G = hq / hkv;
   const int unit = blockIdx.x / G, h = blockIdx.x % G;
   const int b = unit / hkv, g = unit % hkv;

@@ -10,6 +10,23 @@ constexpr int kPage = 16;  // tokens per page
 constexpr int kWave = 64;  // CDNA wavefront width
 constexpr int kXcds = 8;   // MI355X: accelerator dies (XCDs), 32 CUs and one L2 each
 
+// Debug builds (-DFSA_DEBUG_POISON_LDS, libfsa_poison.so) fill a kernel's LDS
+// with a NaN pattern when the kernel starts and where a later stage reuses the
+// LDS of an earlier one, then wait for the whole workgroup: a read of LDS that
+// no stage of the kernel wrote then shows up in the outputs.  Release builds
+// compile this to nothing.
+#ifdef FSA_DEBUG_POISON_LDS
+constexpr int kBuildFlags = 1;
+__device__ __forceinline__ void poison_lds(void* p, size_t bytes) {
+  uint32_t* w = static_cast<uint32_t*>(p);
+  for (size_t i = threadIdx.x; i < bytes / 4; i += blockDim.x) w[i] = 0x7FC07FC0u;  // NaN as fp32 and as bf16
+  __syncthreads();
+}
+#else
+constexpr int kBuildFlags = 0;
+__device__ __forceinline__ void poison_lds(void*, size_t) {}
+#endif
+
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;

@@ -33,6 +33,7 @@ __global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
     int32_t* __restrict__ work, int32_t* __restrict__ counts, int hkv, int max_pages, int prefix,
     int window, int budget, int max_items, int max_seq_len) {
   __shared__ SelectLds S;
+  poison_lds(&S, sizeof(S));
   const int unit = blockIdx.x, b = unit / hkv;
   SelectJob J;
   J.scores = scores + (size_t)unit * max_pages;
@@ -180,6 +181,7 @@ __device__ __forceinline__ void select_and_attend(SelectLds& SL, MergeLds<D, kSe
     my_hi = it.w;
   }
   __syncthreads();  // every read of the selection's LDS precedes the merge that reuses it
+  poison_lds(&SM, sizeof(SM));
   const int n = __popcll(__ballot(my_lo < my_hi));  // a prefix of the wave's lanes
   WaveAttn<D> st;
   if constexpr (kCanPrefetch)
@@ -209,6 +211,9 @@ __global__ __launch_bounds__(kSelThreads) void select_attend_kernel(const StepAr
   } U;
   __shared__ int4 slice[kSliceMax];
   __shared__ bf16x8_t q_lds[D / 32 * kWave];
+  poison_lds(&U, sizeof(U));
+  poison_lds(slice, sizeof(slice));
+  poison_lds(q_lds, sizeof(q_lds));
   const int units = A.batch * A.hkv;
   const int i = blockIdx.x;
   if (i < A.sel_blocks) {

@@ -31,6 +31,12 @@ int32_t fsa_device_memory(int32_t* info, int32_t n_info);
  * arguments. */
 fsa_status fsa_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
+/* How this library was built: bit 0 set in the debug build whose kernels fill
+ * their LDS with a NaN pattern at the start and between stages that reuse it
+ * (libfsa_poison.so, -DFSA_DEBUG_POISON_LDS); 0 in the release build.  Host
+ * only, no device needed. */
+int32_t fsa_build_flags(void);
+
 /* Some of the launches of the fsa_sparse_decode_attn step, so that parts of
  * the step can be timed: runs only launches first..last (0-based, inclusive)
  * of the step these arguments describe.  The launches, in order: dense plan
