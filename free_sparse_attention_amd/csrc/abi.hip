@@ -1,7 +1,10 @@
 // C-ABI entry points declared in include/fsa.h and include/fsa_measure.h: host-side argument checks,
 // workspace layout and launch sequencing on the caller's stream.
+#include <dlfcn.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
 #include <mutex>
@@ -14,6 +17,43 @@
 namespace {
 
 thread_local std::string g_err;
+
+// Optional tracing: with FSA_TRACE=1 in the environment every entry point that
+// launches work opens a roctx range named after itself (rocprofv3
+// --marker-trace shows them beside the kernels).  The roctx library is opened
+// at run time on first use, so libfsa.so has no link-time dependency on it;
+// without FSA_TRACE=1, or without the library, the ranges cost one branch.
+struct Roctx {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+
+const Roctx& roctx() {
+  static const Roctx r = [] {
+    Roctx t;
+    const char* e = getenv("FSA_TRACE");
+    if (e == nullptr || strcmp(e, "1") != 0) return t;
+    void* h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+    if (h == nullptr) h = dlopen("libroctx64.so.4", RTLD_NOW | RTLD_LOCAL);
+    if (h == nullptr) return t;
+    t.push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+    t.pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+    if (t.push == nullptr || t.pop == nullptr) t = Roctx{};
+    return t;
+  }();
+  return r;
+}
+
+struct TraceRange {
+  explicit TraceRange(const char* name) {
+    if (roctx().push) roctx().push(name);
+  }
+  ~TraceRange() {
+    if (roctx().pop) roctx().pop();
+  }
+  TraceRange(const TraceRange&) = delete;
+  TraceRange& operator=(const TraceRange&) = delete;
+};
 
 fsa_status fail(fsa_status st, const char* fmt, ...) {
   char buf[512];
@@ -202,6 +242,7 @@ const char* fsa_last_error(void) { return g_err.c_str(); }
 
 fsa_status fsa_import_kv_plain(const fsa_dims* dims, const void* k_plain, const void* v_plain,
                                void* k_cache, void* v_cache, void* stream) {
+  TraceRange trace("fsa_import_kv_plain");
   FSA_CHECK(check_dims(dims));
   FSA_CHECK(need(k_plain, "k_plain"));
   FSA_CHECK(need(v_plain, "v_plain"));
@@ -218,6 +259,7 @@ fsa_status fsa_import_kv_plain(const fsa_dims* dims, const void* k_plain, const 
 fsa_status fsa_append_kv(const fsa_dims* dims, int32_t n_new, const void* k_new, const void* v_new,
                          const int32_t* page_table, const int32_t* seq_lens, int32_t* seq_lens_out,
                          void* k_cache, void* v_cache, void* meta, void* stream) {
+  TraceRange trace("fsa_append_kv");
   FSA_CHECK(check_dims(dims));
   if (n_new < 1) return fail(FSA_ERR_INVALID_ARG, "n_new must be >= 1");
   FSA_CHECK(need(k_new, "k_new"));
@@ -240,6 +282,7 @@ fsa_status fsa_append_kv(const fsa_dims* dims, int32_t n_new, const void* k_new,
 
 fsa_status fsa_build_page_meta(const fsa_dims* dims, const void* k_cache, const int32_t* page_table,
                                const int32_t* seq_lens, void* meta, void* stream) {
+  TraceRange trace("fsa_build_page_meta");
   FSA_CHECK(check_dims(dims));
   FSA_CHECK(need(k_cache, "k_cache"));
   FSA_CHECK(need(page_table, "page_table"));
@@ -257,6 +300,7 @@ fsa_status fsa_build_page_meta(const fsa_dims* dims, const void* k_cache, const 
 fsa_status fsa_quest_scores(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len,
                             const void* q, const void* meta, const int32_t* seq_lens, float* scores,
                             void* stream) {
+  TraceRange trace("fsa_quest_scores");
   FSA_CHECK(check_dims(dims));
   FSA_CHECK(check_cfg(cfg));
   FSA_CHECK(check_len(dims, max_seq_len));
@@ -287,6 +331,7 @@ int32_t fsa_max_work_items(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_
 fsa_status fsa_select_pages(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len,
                             const float* scores, const int32_t* page_table, const int32_t* seq_lens,
                             int32_t* sel_pages, int32_t* work, int32_t* counts, void* stream) {
+  TraceRange trace("fsa_select_pages");
   FSA_CHECK(check_dims(dims));
   FSA_CHECK(check_cfg(cfg));
   FSA_CHECK(check_len(dims, max_seq_len));
@@ -460,6 +505,7 @@ fsa_status fsa_sparse_decode_attn(const fsa_dims* dims, fsa_layer_cfg cfg, float
                                   const void* v_cache, const void* meta, const int32_t* page_table,
                                   const int32_t* seq_lens, void* out, int32_t* sel_pages,
                                   void* workspace, size_t workspace_bytes, void* stream) {
+  TraceRange trace("fsa_sparse_decode_attn");
   FSA_CHECK(check_step(dims, cfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table, seq_lens, out,
                        workspace, workspace_bytes));
   return run_sparse_step(dims, cfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table, seq_lens, out,
@@ -470,6 +516,7 @@ fsa_status fsa_sparse_decode_attn_noalloc(const fsa_dims* dims, fsa_layer_cfg cf
                                           int32_t max_seq_len, const void* q, const void* k_cache,
                                           const void* v_cache, const void* meta, const int32_t* page_table,
                                           const int32_t* seq_lens, void* out, int32_t* sel_pages, void* stream) {
+  TraceRange trace("fsa_sparse_decode_attn_noalloc");
   // every host check, the size limit included, before any HIP call
   FSA_CHECK(check_step_args(dims, cfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table, seq_lens, out));
   const size_t total = sparse_ws(dims, cfg, max_seq_len).total;
@@ -489,6 +536,7 @@ fsa_status fsa_append_decode_attn(const fsa_dims* dims, int32_t n_new, const voi
                                   float sm_scale, int32_t max_seq_len, const void* q, void* k_cache,
                                   void* v_cache, void* meta, const int32_t* page_table, void* out,
                                   int32_t* sel_pages, void* workspace, size_t workspace_bytes, void* stream) {
+  TraceRange trace("fsa_append_decode_attn");
   FSA_CHECK(check_step(dims, cfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table, seq_lens_out, out,
                        workspace, workspace_bytes));
   if (n_new < 1) return fail(FSA_ERR_INVALID_ARG, "n_new must be >= 1");
@@ -509,6 +557,7 @@ int32_t fsa_sparse_decode_attn_launches(const fsa_dims* dims, fsa_layer_cfg cfg,
                                         const void* meta, const int32_t* page_table, const int32_t* seq_lens,
                                         void* out, int32_t* sel_pages, void* workspace, size_t workspace_bytes,
                                         int32_t first, int32_t last, void* stream) {
+  TraceRange trace("fsa_sparse_decode_attn_launches");
   if (check_step(dims, cfg, sm_scale, max_seq_len, q, k_cache, v_cache, meta, page_table, seq_lens, out, workspace,
                  workspace_bytes) != FSA_OK)
     return -1;
@@ -573,6 +622,7 @@ int32_t fsa_device_memory(int32_t* info, int32_t n_info) {
 }
 
 fsa_status fsa_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  TraceRange trace("fsa_read_probe");
   FSA_CHECK(need(buf, "buf"));
   FSA_CHECK(need(sink, "sink"));
   if (bytes == 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
@@ -589,6 +639,7 @@ fsa_status fsa_dense_decode_attn(const fsa_dims* dims, float sm_scale, int32_t m
                                  const void* q, const void* k_cache, const void* v_cache,
                                  const int32_t* page_table, const int32_t* seq_lens, void* out,
                                  void* workspace, size_t workspace_bytes, void* stream) {
+  TraceRange trace("fsa_dense_decode_attn");
   FSA_CHECK(check_dims(dims));
   FSA_CHECK(check_len(dims, max_seq_len));
   FSA_CHECK(need(q, "q"));
@@ -611,6 +662,7 @@ fsa_status fsa_dense_decode_attn(const fsa_dims* dims, float sm_scale, int32_t m
 fsa_status fsa_validate_inputs(const fsa_dims* dims, int32_t n_new, int32_t max_seq_len, const void* q,
                                const int32_t* page_table, const int32_t* seq_lens, int32_t* scratch,
                                void* stream) {
+  TraceRange trace("fsa_validate_inputs");
   FSA_CHECK(check_dims(dims));
   FSA_CHECK(check_len(dims, max_seq_len));
   if (n_new < 0) return fail(FSA_ERR_INVALID_ARG, "n_new must be >= 0");

@@ -229,3 +229,30 @@ def test_launch_range_call_checks_its_arguments(lib):
     assert lib.fsa_sparse_decode_attn_launches(ctypes.byref(d), c, 0.1, 4096, p, p, p, p, p, p, p, None, p, need - 1,
                                                0, 0, None) == -1
     assert b"workspace" in lib.fsa_last_error()
+
+
+@pytest.mark.parametrize("trace", ["1", None])
+def test_trace_ranges_open_roctx_only_on_request(trace):
+    """FSA_TRACE=1 makes the entry points open roctx ranges: the roctx library is
+    loaded at run time on the first traced call (here one that fails its
+    argument check before any launch); without it nothing is loaded."""
+    import subprocess
+    import sys
+    code = (
+        "import sys\n"
+        f"sys.path.insert(0, {os.path.dirname(os.path.dirname(os.path.abspath(__file__)))!r})\n"
+        "from free_sparse_attention_amd import _lib\n"
+        "L = _lib.load()\n"
+        "rc = L.fsa_quest_scores(None, _lib.LayerCfg(0, 0, 0), 0, None, None, None, None, None)\n"
+        "maps = open('/proc/self/maps').read()\n"
+        "print(rc, int('rocprofiler-sdk-roctx' in maps))\n")
+    env = {k: v for k, v in os.environ.items() if k != "FSA_TRACE"}
+    if trace:
+        env["FSA_TRACE"] = trace
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    rc, loaded = r.stdout.split()
+    assert int(rc) == _lib.FSA_ERR_INVALID_ARG
+    if trace and not os.path.exists("/opt/rocm/lib/librocprofiler-sdk-roctx.so.1"):
+        pytest.skip("no roctx library in this ROCm install")
+    assert int(loaded) == (1 if trace else 0)
