@@ -45,6 +45,8 @@ def build(verbose: bool = False) -> str:
         so, se = p.communicate()
         if p.returncode != 0:
             failed.append(f"{os.path.basename(out)}: hipcc failed ({p.returncode}):\n{so}\n{se}")
+            if os.path.exists(tmp):
+                os.remove(tmp)
         else:
             os.replace(tmp, out)
     if failed:
