@@ -317,9 +317,10 @@ StepPlan plan_step(int units, int head_dim, int prefix, int window, int budget, 
   p.sel_blocks = p.xcd_grouped ? kXcds * per_xcd : busy;
   // prefetch of known-taken pages into the shared L2 while it holds them
   // comfortably: the K and V blocks of one XCD's units' selections within
-  // half of its 4 MiB
+  // half of its 4 MiB, and at most 8 pages per selection thread (beyond, the
+  // registers go to the keys and the second selected page)
   const long xcd_bytes = (long)((units + kXcds - 1) / kXcds) * p.sel_items * 2 * kPage * head_dim * 2;
-  p.prefetch = p.xcd_grouped && xcd_bytes <= (2l << 20);
+  p.prefetch = p.xcd_grouped && xcd_bytes <= (2l << 20) && select_cols(max_seq_len) <= 8;
   return p;
 }
 

@@ -260,6 +260,22 @@ def test_longest_contexts_32_pages_per_thread():
     run_and_check(wl, dense=False)
 
 
+@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 8), (128, 16, 1)], ids=["d64-g1", "d128-g16"])
+def test_two_selected_pages_per_wave_at_16_pages_per_thread(d, hq, hkv):
+    """Over 8192 pages the replicas copy the query operand into LDS (head
+    columns past the group repeat its last head) and keep both of a wave's two
+    selected pages in flight: checked at D 64 with one head per group and at
+    D 128 with sixteen."""
+    import free_sparse_attention_amd as fsa
+    wl = synth.workloads.build(name=f"two{d}_{hq}_{hkv}", seed=23, batch=16 // hkv, hq=hq, hkv=hkv, d=d,
+                               seq_lens=tuple(140000 - 9001 * i for i in range(16 // hkv)), prefix=64, window=2048,
+                               budget=256, k_sigma=0.5, n_needles=8, permuted=True)
+    dw = DeviceWorkload(wl)
+    plan = fsa.describe_step(dw.dims, dw.cfg(), dw.max_seq_len)
+    assert plan["plan"] == "wide" and plan["select_cols"] == 16 and plan["per_replica"] == 32, plan
+    run_and_check(wl, dw=dw, dense=False)
+
+
 @pytest.mark.parametrize("cfg", [(0, 0, 5), (0, 300, 0), (100, 0, 0), (37, 53, 6), (64, 256, 10**5),
                                  (5000, 16, 3), (16, 5000, 3), (0, 1, 1)])
 def test_configs_and_degenerate_regions(cfg):
