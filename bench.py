@@ -31,6 +31,49 @@ HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
+
+
+class HipEvent:
+    """A HIP timing event created with flags (torch's events take none)."""
+    _hip = None
+
+    def __init__(self, flags: int):
+        import ctypes
+        if HipEvent._hip is None:
+            # the HIP runtime the process already uses (torch's), not a second copy
+            with open("/proc/self/maps") as f:
+                path = next((ln.split()[-1] for ln in f if "libamdhip64" in ln), "libamdhip64.so")
+            h = ctypes.CDLL(path)
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipEvent._hip = h
+        self._ev = ctypes.c_void_p()
+        if HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self._ev), flags) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream) -> None:
+        import ctypes
+        if HipEvent._hip.hipEventRecord(self._ev, ctypes.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        if HipEvent._hip.hipEventElapsedTime(ctypes.byref(ms), self._ev, end._ev) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        try:
+            if HipEvent._hip is not None and self._ev:
+                HipEvent._hip.hipEventDestroy(self._ev)
+        except Exception:  # interpreter shutdown
+            pass
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -283,9 +326,10 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
     ms_score = timed(score, n_k, 10)
 
     # each launch of the step timed live with HIP events on the step's
-    # stream, in its place in the step: the prefix of launches 0..j is timed
-    # over at least 200 rotated steps, and launch j is charged the difference
-    # between prefixes j and j - 1 (so the launches add up to the step)
+    # stream, in its place in the step.  Its share of the step: the prefix of
+    # launches 0..j is timed over at least 200 rotated steps, and launch j is
+    # charged the difference between prefixes j and j - 1 (so the shares add
+    # up to the step; the boundary before a launch is charged to it)
     plan = fsa.describe_step(base.dims, c, msl)["plan"]
     names = LAUNCHES[plan]
     step(0)
@@ -307,12 +351,13 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
             pre[j] += timed(prefix_fn(j), n_l // rounds, 10) / rounds
     per = [pre[0]] + [max(1e-6, pre[j] - pre[j - 1]) for j in range(1, len(names))]
 
-    # cross-check: every launch of as many rotated steps bracketed by its own
-    # pair of HIP events on the step's stream (the event markers add about
-    # 1.5-2.5 us to each launch, so this overstates a launch's duration)
-    def bracketed(n, w):
-        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
-              for _ in range(n)]
+    # and each launch's own duration: every launch of at least 200 rotated
+    # steps bracketed by its own pair of HIP events on the step's stream.  The
+    # events are created without the system-scope fence (a default event's
+    # marker writes caches back for the host and adds 1.5-2.5 us to the span);
+    # the spans then match what a kernel trace reports per dispatch.
+    def bracketed(n, w, flags):
+        ev = [[(HipEvent(flags), HipEvent(flags)) for _ in names] for _ in range(n)]
         for i in range(w + n):
             k, v, m = reps[i % R]
             for j in range(len(names)):
@@ -323,13 +368,15 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
                 if i >= w:
                     ev[i - w][j][1].record(stream)
         torch.cuda.synchronize()
-        return [sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(n)) / n for j in range(len(names))]
+        return [sum(ev[i][j][0].elapsed_ms(ev[i][j][1]) for i in range(n)) / n for j in range(len(names))]
 
-    own = bracketed(n_l, 10)
+    own = bracketed(n_l, 10, HIP_EVENT_DISABLE_SYSTEM_FENCE)
+    fenced = bracketed(n_l, 10, 0)
     lb = launch_bytes(wl, plan)
-    launches = [{"kernel": names[j], "avg_launch_us": 1000.0 * per[j], "alg_bytes": lb[j],
-                 "achieved_GBps": lb[j] / (per[j] * 1e-3) / 1e9, "frac": lb[j] / (per[j] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                 "bracketed_us": 1000.0 * own[j], "time_share": per[j] / sum(per)} for j in range(len(names))]
+    launches = [{"kernel": names[j], "avg_launch_us": 1000.0 * own[j], "alg_bytes": lb[j],
+                 "achieved_GBps": lb[j] / (own[j] * 1e-3) / 1e9, "frac": lb[j] / (own[j] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "marginal_us": 1000.0 * per[j], "fenced_events_us": 1000.0 * fenced[j],
+                 "time_share": per[j] / sum(per)} for j in range(len(names))]
     marked_ms = sum(per)
 
     res = {"ms_per_step": ms_step, "steps_per_s": 1000.0 / ms_step, "step_alg_bytes": step_bytes,
