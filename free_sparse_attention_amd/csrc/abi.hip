@@ -459,6 +459,10 @@ fsa_status run_sparse_step(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_sca
   sa.xcd_grouped = w.step.xcd_grouped;
   sa.prefetch = w.step.prefetch;
   sa.scale_log2 = sm_scale * 1.4426950408889634f;
+  sa.G = dims->num_q_heads / dims->num_kv_heads;
+  sa.by_hkv = fsa::make_fastdiv((uint32_t)dims->num_kv_heads);
+  sa.by_rep = fsa::make_fastdiv((uint32_t)std::max(1, sa.sel_rep));
+  sa.by_pw = fsa::make_fastdiv((uint32_t)std::max(1, sa.pw_wg));
   if (mk.take()) FSA_CHECK(hip_status(fsa::launch_select_attend(sa, st), "selection launch"));
   fsa::AttnArgs a = attn_args(dims, w.step.sel_items, sm_scale, max_seq_len, q, k_cache, v_cache, page_table, seq_lens,
                               at<int32_t>(workspace, w.sel_work), at<float>(workspace, w.part_o),

@@ -30,12 +30,13 @@ __global__ __launch_bounds__(256, 3) void decode_attention_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ work,
     float* __restrict__ part_o, float* __restrict__ part_ml,
     uint16_t* __restrict__ out, int hq, int hkv, int max_pages, int max_items, int ipw,
-    int wg_per_unit, int slots_per_unit, int slot_base, float scale_log2, int max_seq_len) {
+    int wg_per_unit, int slots_per_unit, int slot_base, float scale_log2, int max_seq_len, FastDiv by_wg,
+    FastDiv by_hkv, int G) {
   __shared__ MergeLds<D, kAttnWaves> S;
   poison_lds(&S, sizeof(S));
 
-  const int unit = blockIdx.x / wg_per_unit, wg = blockIdx.x % wg_per_unit;
-  const int b = unit / hkv, g = unit % hkv, G = hq / hkv;
+  const int unit = (int)fdiv(blockIdx.x, by_wg), wg = (int)blockIdx.x - unit * wg_per_unit;
+  const int b = (int)fdiv((uint32_t)unit, by_hkv), g = unit - b * hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int per_wg = kAttnWaves * ipw;
   const int i_begin = wg * per_wg + wave * ipw;
@@ -89,7 +90,7 @@ template <int D, int MODE>
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, uint16_t* __restrict__ out, int hq, int hkv, int per_wg, int slots_per_unit,
-    int max_seq_len) {
+    int max_seq_len, FastDiv by_g, FastDiv by_hkv) {
   constexpr int NQ = D / 4;        // float4 columns of one head
   constexpr int PARTS = 256 / NQ;  // threads sharing a column, each with every PARTS-th partial
   __shared__ float sh_m[PARTS][NQ], sh_l[PARTS][NQ];
@@ -97,9 +98,9 @@ __global__ __launch_bounds__(256) void combine_kernel(
   poison_lds(sh_m, sizeof(sh_m));
   poison_lds(sh_l, sizeof(sh_l));
   poison_lds(sh_acc, sizeof(sh_acc));
-  const int G = hq / hkv;
-  const int unit = blockIdx.x / G, h = blockIdx.x % G;
-  const int b = unit / hkv, g = unit % hkv;
+  const int G = (int)by_g.d;
+  const int unit = (int)fdiv(blockIdx.x, by_g), h = (int)blockIdx.x - unit * G;
+  const int b = (int)fdiv((uint32_t)unit, by_hkv), g = unit - b * hkv;
   // partial slots in use: all of them for the decode step's partials (empty
   // ones carry m = -inf); dense units use as many as their length needs
   int n = slots_per_unit;
@@ -184,10 +185,12 @@ AttnPlan plan_attention(int units, int max_items) {
 hipError_t launch_combine(const AttnArgs& a, int slots, hipStream_t stream) {
   if (a.d == 128)
     hipLaunchKernelGGL((combine_kernel<128, kList>), dim3((unsigned)(a.batch * a.hq)), dim3(256), 0, stream, a.part_o,
-                       a.part_ml, a.seq_lens, a.out, a.hq, a.hkv, 1, slots, a.max_seq_len);
+                       a.part_ml, a.seq_lens, a.out, a.hq, a.hkv, 1, slots, a.max_seq_len,
+                       make_fastdiv((uint32_t)(a.hq / a.hkv)), make_fastdiv((uint32_t)a.hkv));
   else
     hipLaunchKernelGGL((combine_kernel<64, kList>), dim3((unsigned)(a.batch * a.hq)), dim3(256), 0, stream, a.part_o,
-                       a.part_ml, a.seq_lens, a.out, a.hq, a.hkv, 1, slots, a.max_seq_len);
+                       a.part_ml, a.seq_lens, a.out, a.hq, a.hkv, 1, slots, a.max_seq_len,
+                       make_fastdiv((uint32_t)(a.hq / a.hkv)), make_fastdiv((uint32_t)a.hkv));
   return hipGetLastError();
 }
 
@@ -203,11 +206,13 @@ hipError_t launch_attention(AttnMode mode, const AttnPlan& plan, const AttnArgs&
       hipLaunchKernelGGL((decode_attention_kernel<DD, MM>), grid, dim3(256), 0, stream, a.q, a.kc, a.vc, \
                          a.page_table, a.seq_lens, a.work, a.part_o, a.part_ml, a.out, a.hq, a.hkv,       \
                          a.max_pages, a.max_items, plan.items_per_wave, plan.wg_per_unit, slots, base,    \
-                         a.scale_log2, a.max_seq_len);                                                     \
+                         a.scale_log2, a.max_seq_len, make_fastdiv((uint32_t)plan.wg_per_unit),            \
+                         make_fastdiv((uint32_t)a.hkv), a.hq / a.hkv);                                    \
     if (slots > 1 && (!filter || filter->take()))                                                         \
       hipLaunchKernelGGL((combine_kernel<DD, MM>), dim3((unsigned)(a.batch * a.hq)), dim3(256), 0, stream, \
                          a.part_o, a.part_ml, a.seq_lens, a.out, a.hq, a.hkv,                             \
-                         kAttnWaves * plan.items_per_wave, slots, a.max_seq_len);                         \
+                         kAttnWaves * plan.items_per_wave, slots, a.max_seq_len,                          \
+                         make_fastdiv((uint32_t)(a.hq / a.hkv)), make_fastdiv((uint32_t)a.hkv));          \
   } while (0)
   if (a.d == 128) {
     if (mode == kDense) FSA_ATTN(128, kDense); else FSA_ATTN(128, kList);

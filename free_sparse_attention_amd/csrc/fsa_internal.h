@@ -187,6 +187,24 @@ hipError_t launch_validate(const uint16_t* q, const int32_t* page_table, const i
 // One decode step's selection launch: the top-k selection of every (sequence,
 // KV head) with the attention over the selected pages, plus the attention over
 // the prefix and window pages.
+// Division by a launch-invariant divisor without the reciprocal sequence a
+// runtime division compiles to: m = min(floor(2^32 / d), 2^32 - 1) makes
+// umulhi(n, m) equal n / d or one less for every 32-bit n (d >= 1), and one
+// compare settles it (Granlund and Montgomery, "Division by invariant
+// integers using multiplication", 1994).  The host fills d and m.
+struct FastDiv {
+  uint32_t d, m;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  const uint64_t m = (uint64_t{1} << 32) / (d ? d : 1);
+  return FastDiv{d, (uint32_t)(m > 0xFFFFFFFFull ? 0xFFFFFFFFull : m)};
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  uint32_t q = __umulhi(n, f.m);
+  if (n - q * f.d >= f.d) ++q;
+  return q;
+}
+
 struct StepArgs {
   const float* scores;        // [B][Hkv][max_pages] Quest scores
   const int32_t* page_table;  // [B][max_pages]
@@ -213,6 +231,8 @@ struct StepArgs {
   int xcd_grouped;     // wide plan: workgroup -> (unit, replica) keeps a unit on one XCD
   int prefetch;        // wide plan: replicas prefetch known-taken pages into their L2
   float scale_log2;
+  int G;                          // hq / hkv
+  FastDiv by_hkv, by_rep, by_pw;  // divisions by hkv, sel_rep (or 1), pw_wg (or 1)
 };
 
 // Prefix/window attention plan: at most max_items items per unit, ipw per wave,

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(W * 64) void quest_score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ meta,
     const int32_t* __restrict__ seq_lens, float* __restrict__ scores, int hq, int hkv,
     int max_pages, int prefix, int window, int tiles_per_wave, int wg_per_unit, int max_seq_len,
-    const AppendArgs ap, int append_blocks, int append_tasks, int len_add) {
+    const AppendArgs ap, int append_blocks, int append_tasks, int len_add, FastDiv by_wg, FastDiv by_hkv, int G) {
   constexpr int NSTEP = 2 * D / 32;  // k-steps over the 2D metadata values
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if ((int)blockIdx.x < append_blocks) {
@@ -66,8 +66,8 @@ __global__ __launch_bounds__(W * 64) void quest_score_kernel(
     return;
   }
   const int blk = (int)blockIdx.x - append_blocks;
-  const int unit = blk / wg_per_unit, wg = blk % wg_per_unit;
-  const int b = unit / hkv, g = unit % hkv, G = hq / hkv;
+  const int unit = (int)fdiv((uint32_t)blk, by_wg), wg = blk - unit * wg_per_unit;
+  const int b = (int)fdiv((uint32_t)unit, by_hkv), g = unit - b * hkv;
   const int col = lane & 15, gq = lane >> 4;
   // Every sequence with candidates has L > prefix, so its candidates start at
   // page prefix / 16 and end at or before the host bound's: the wave's first
@@ -194,7 +194,7 @@ hipError_t launch_quest_scores(const uint16_t* q, const uint16_t* meta, const in
 #define FSA_SCORE(DD, WW)                                                                                       \
   hipLaunchKernelGGL((quest_score_kernel<DD, WW>), grid, dim3(WW * 64), 0, stream, q, meta, seq_lens, scores, hq, \
                      hkv, max_pages, prefix, window, tpw, wg_per_unit, max_seq_len, ap, append_blocks, append_tasks,  \
-                     len_add)
+                     len_add, make_fastdiv((uint32_t)wg_per_unit), make_fastdiv((uint32_t)hkv), hq / hkv)
   if (d == 128) {
     if (W == 8) FSA_SCORE(128, 8); else FSA_SCORE(128, 4);
   } else {

@@ -81,7 +81,7 @@ __device__ __forceinline__ bool prefix_window_item(int i, int L, int prefix, int
 template <int D>
 __device__ __forceinline__ void prefix_window_attend(MergeLds<D, kSelWaves>& S, const StepArgs& A, int unit,
                                                      int wg) {
-  const int b = unit / A.hkv, g = unit % A.hkv, G = A.hq / A.hkv;
+  const int b = (int)fdiv((uint32_t)unit, A.by_hkv), g = unit - b * A.hkv, G = A.G;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane < A.pw_ipw ? (wg * kSelWaves + wave) * A.pw_ipw + lane : -1;
   const int32_t* pt = A.page_table + (size_t)b * A.max_pages;
@@ -106,7 +106,7 @@ __device__ __forceinline__ void prefix_window_attend(MergeLds<D, kSelWaves>& S, 
 }
 
 __device__ __forceinline__ SelectJob step_job(const StepArgs& A, int unit) {
-  const int b = unit / A.hkv;
+  const int b = (int)fdiv((uint32_t)unit, A.by_hkv);
   SelectJob J;
   J.scores = A.scores + (size_t)unit * A.max_pages;
   J.pt = A.page_table + (size_t)b * A.max_pages;
@@ -141,7 +141,7 @@ __device__ __forceinline__ SelectJob step_job(const StepArgs& A, int unit) {
 template <int COLS, int D>
 __device__ __forceinline__ void select_and_attend(SelectLds& SL, MergeLds<D, kSelWaves>& SM, int4* slice,
                                                   bf16x8_t* q_lds, const StepArgs& A, int unit, int r) {
-  const int b = unit / A.hkv, g = unit % A.hkv, G = A.hq / A.hkv;
+  const int b = (int)fdiv((uint32_t)unit, A.by_hkv), g = unit - b * A.hkv, G = A.G;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // the query operand is loaded first, so that waiting for it later does not
   // wait for the selection's prefetch loads (loads complete in order)
@@ -218,11 +218,12 @@ __global__ __launch_bounds__(kSelThreads) void select_attend_kernel(const StepAr
   const int i = blockIdx.x;
   if (i < A.sel_blocks) {
     if (A.sel_rep > 0) {
-      int unit = i / A.sel_rep, r = i % A.sel_rep;
+      int unit = (int)fdiv((uint32_t)i, A.by_rep), r = i - unit * A.sel_rep;
       if (A.xcd_grouped) {
         const int k = i / kXcds;
-        unit = i % kXcds + kXcds * (k / A.sel_rep);
-        r = k % A.sel_rep;
+        const int kq = (int)fdiv((uint32_t)k, A.by_rep);
+        unit = i % kXcds + kXcds * kq;
+        r = k - kq * A.sel_rep;
         if (unit >= units) return;
       }
       select_and_attend<COLS, D>(U.sel, U.att, slice, q_lds, A, unit, r);
@@ -236,7 +237,8 @@ __global__ __launch_bounds__(kSelThreads) void select_attend_kernel(const StepAr
     }
   } else {
     const int w = i - A.sel_blocks;
-    prefix_window_attend<D>(U.att, A, w / A.pw_wg, w % A.pw_wg);
+    const int pu = (int)fdiv((uint32_t)w, A.by_pw);
+    prefix_window_attend<D>(U.att, A, pu, w - pu * A.pw_wg);
   }
 }
 
