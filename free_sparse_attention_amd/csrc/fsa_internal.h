@@ -199,8 +199,8 @@ inline FastDiv make_fastdiv(uint32_t d) {
   const uint64_t m = (uint64_t{1} << 32) / (d ? d : 1);
   return FastDiv{d, (uint32_t)(m > 0xFFFFFFFFull ? 0xFFFFFFFFull : m)};
 }
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
-  uint32_t q = __umulhi(n, f.m);
+__host__ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  uint32_t q = (uint32_t)(((uint64_t)n * f.m) >> 32);  // a multiply-high on the device
   if (n - q * f.d >= f.d) ++q;
   return q;
 }

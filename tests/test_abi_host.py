@@ -256,3 +256,45 @@ def test_trace_ranges_open_roctx_only_on_request(trace):
     if trace and not os.path.exists("/opt/rocm/lib/librocprofiler-sdk-roctx.so.1"):
         pytest.skip("no roctx library in this ROCm install")
     assert int(loaded) == (1 if trace else 0)
+
+
+def test_fast_division_is_exact(tmp_path):
+    """The kernels' division by launch-invariant divisors (fsa_internal.h
+    make_fastdiv / fdiv), built for the host with hipcc: equal to n / d for
+    every 16-bit numerator at divisors 1..1024 and for edge and random 32-bit
+    numerators at divisors up to 2^32 - 1."""
+    import subprocess
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc is not installed")
+    csrc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "free_sparse_attention_amd",
+                        "csrc")
+    src = tmp_path / "fastdiv.cpp"
+    src.write_text(r'''
+#include <cstdio>
+#include <cstdint>
+#include "fsa_internal.h"
+int main() {
+  uint64_t bad = 0, s = 88172645463325252ull;
+  auto next = [&]() { s ^= s << 13; s ^= s >> 7; s ^= s << 17; return (uint32_t)s; };
+  for (uint32_t d = 1; d <= 1024; ++d) {
+    const fsa::FastDiv f = fsa::make_fastdiv(d);
+    for (uint32_t n = 0; n < 65536; ++n) bad += fsa::fdiv(n, f) != n / d;
+  }
+  const uint32_t ds[] = {1, 2, 3, 7, 8, 100, 65535, 65536, 65537, 1u << 20, 2147483647u, 2147483648u, 4294967295u};
+  for (uint32_t d : ds) {
+    const fsa::FastDiv f = fsa::make_fastdiv(d);
+    const uint32_t edge[] = {0, 1, d - 1, d, d + 1, 2 * d - 1, 4294967295u, 4294967294u};
+    for (uint32_t n : edge) bad += fsa::fdiv(n, f) != n / d;
+    for (int i = 0; i < 1000000; ++i) { const uint32_t n = next(); bad += fsa::fdiv(n, f) != n / d; }
+  }
+  printf("%llu\n", (unsigned long long)bad);
+  return 0;
+}
+''')
+    exe = tmp_path / "fastdiv"
+    r = subprocess.run([hipcc, "-O2", "-std=c++17", "-x", "hip", "--offload-arch=gfx950", "-I", csrc, "-o", str(exe),
+                        str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0 and out.stdout.strip() == "0", (out.stdout, out.stderr[-500:])
