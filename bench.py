@@ -150,6 +150,7 @@ def launch_bytes(wl, plan):
 # the sources each kernel is compiled from (a counter record holds their hash)
 KERNEL_SOURCES = {
     "quest_score_kernel": ["free_sparse_attention_amd/csrc/quest_score.hip",
+                           "free_sparse_attention_amd/csrc/score_core.h",
                            "free_sparse_attention_amd/csrc/append_core.h",
                            "free_sparse_attention_amd/csrc/fsa_internal.h"],
     "select_attend_kernel": ["free_sparse_attention_amd/csrc/select_pages.hip",
@@ -301,6 +302,14 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
                                out, None, ws, stream)
 
     warm_ms = timed(warm_step, max(steps, 100), max(warmup, 10))
+    # the one-launch form of the wide plan (off by default), same rotation
+    one_us = None
+    old = fsa.set_one_launch(1)
+    try:
+        if fsa.describe_step(base.dims, c, msl).get("one_launch"):
+            one_us = 1000.0 * timed(step, max(steps, 100), max(warmup, 10))
+    finally:
+        fsa.set_one_launch(old)
     # cold: single steps, each after a 1 GiB scrub that evicts L2 and the Infinity Cache
     scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     cold_us = []
@@ -386,7 +395,8 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
            "replicas": R, "warm_mall_step_us": 1000.0 * warm_ms,
            "repetitions": {"reps": 20, "steps_each": 50, "median_us": reps_us[10], "p10_us": reps_us[2],
                            "p90_us": reps_us[18]},
-           "cold_single_step_us": {"median": cold_us[10], "p10": cold_us[2], "p90": cold_us[18]}}
+           "cold_single_step_us": {"median": cold_us[10], "p10": cold_us[2], "p90": cold_us[18]},
+           "one_launch_step_us": one_us}
     if with_dense:
         dws = base.dense_workspace()
 
@@ -784,6 +794,7 @@ def main():
         "cpu_baseline": cpu,
         "repetitions": r["repetitions"],
         "cold_single_step_us": r["cold_single_step_us"],
+        "one_launch_step_us": r["one_launch_step_us"],
         "also": {},
         "detail": {k: v for k, v in r.items()},
     }
@@ -799,7 +810,8 @@ def main():
                                "speedup_vs_dense": v.get("speedup_vs_dense"), "plan": v["plan"],
                                "launches": v["launches"], "score_GBps": v["score_GBps"],
                                "warm_mall_step_us": v["warm_mall_step_us"], "repetitions": v["repetitions"],
-                               "cold_single_step_us": v["cold_single_step_us"]}
+                               "cold_single_step_us": v["cold_single_step_us"],
+                               "one_launch_step_us": v["one_launch_step_us"]}
     print(json.dumps(line), flush=True)
 
 

@@ -24,6 +24,8 @@ from ._lib import (  # noqa: F401
     meta_bytes,
     quest_scores,
     read_probe,
+    one_launch_stalls,
+    set_one_launch,
     build_flags,
     select_pages,
     sparse_decode_attn,

@@ -27,7 +27,7 @@ EXPORTED = (
     "fsa_sparse_decode_workspace_bytes", "fsa_sparse_decode_attn",
     "fsa_dense_decode_workspace_bytes", "fsa_dense_decode_attn", "fsa_validate_inputs", "fsa_describe_step",
     "fsa_append_decode_attn", "fsa_device_memory", "fsa_read_probe", "fsa_sparse_decode_attn_noalloc",
-    "fsa_sparse_decode_attn_launches", "fsa_build_flags",
+    "fsa_sparse_decode_attn_launches", "fsa_build_flags", "fsa_set_one_launch", "fsa_one_launch_stalls",
 )
 
 
@@ -110,6 +110,8 @@ def _open(path: str) -> ctypes.CDLL:
         "fsa_device_memory": (i32, [ctypes.POINTER(i32), i32]),
         "fsa_read_probe": (i32, [vp, sz, vp, vp]),
         "fsa_build_flags": (i32, []),
+        "fsa_set_one_launch": (i32, [i32]),
+        "fsa_one_launch_stalls": (i32, [ctypes.POINTER(ctypes.c_int64)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -186,7 +188,7 @@ def quest_scores(d: Dims, c: LayerCfg, max_seq_len, q, meta, seq_lens, scores, s
 
 
 STEP_INFO = ("plan", "replicas", "per_replica", "xcd_grouped", "prefetch", "pw_workgroups", "slots", "select_cols",
-             "pw_items_per_wave")
+             "pw_items_per_wave", "one_launch", "score_tasks")
 PLANS = {0: "dense", 1: "wide", 2: "narrow"}
 
 
@@ -216,6 +218,21 @@ def device_memory() -> dict:
 def build_flags() -> int:
     """fsa_build_flags of the library in use: bit 0 = LDS-poison debug build."""
     return int(load().fsa_build_flags())
+
+
+def set_one_launch(mode: int) -> int:
+    """When the one-launch form of the wide plan is used (process-wide): 0
+    never (the default), 1 for unit counts that are multiples of 8, 2 wherever
+    it applies.  Returns the previous mode."""
+    return int(load().fsa_set_one_launch(int(mode)))
+
+
+def one_launch_stalls() -> int:
+    """Waits the one-launch kernel gave up on since the library was loaded
+    (nonzero: some step's result is wrong).  Synchronises the device."""
+    n = ctypes.c_int64(0)
+    _check(load().fsa_one_launch_stalls(ctypes.byref(n)))
+    return int(n.value)
 
 
 def read_probe(buf, sink, stream=None):

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <string>
 
@@ -152,13 +153,23 @@ struct SparseWs {
   bool all_taken;
   fsa::StepPlan step;
   fsa::AttnPlan plan;  // dense plan (all candidates taken) or split-K plan (narrow)
+  bool one;            // wide plan as one launch; `one_launch` holds its task sizes
+  fsa::OneLaunchArgs one_launch;
 };
+
+// When the one-launch form of the wide plan is used (fsa_set_one_launch): 0
+// never (the default: it measured slower than the separate launches at 4k to
+// 256k tokens), 1 where it applies and the units spread evenly over the XCDs,
+// 2 wherever it applies.
+std::atomic<int> g_one_launch_mode{0};
 
 SparseWs sparse_ws(const fsa_dims* d, fsa_layer_cfg c, int32_t max_seq_len) {
   SparseWs w;
   const int units = d->batch * d->num_kv_heads;
   const int G = d->num_q_heads / d->num_kv_heads;
   w.all_taken = candidate_pages(c, max_seq_len) <= c.budget_pages;
+  w.one = false;
+  w.one_launch = fsa::OneLaunchArgs{};
   size_t o = 0;
   w.scores = o;   o = align256(o + (size_t)units * d->max_pages_per_seq * sizeof(float));
   w.sel_work = o;
@@ -168,6 +179,8 @@ SparseWs sparse_ws(const fsa_dims* d, fsa_layer_cfg c, int32_t max_seq_len) {
     w.slots = w.plan.wg_per_unit;
   } else {
     w.step = fsa::plan_step(units, d->head_dim, c.prefix_tokens, c.window_tokens, c.budget_pages, max_seq_len);
+    w.one = fsa::plan_one_launch(w.step, units, d->head_dim, G, c.prefix_tokens, c.window_tokens, max_seq_len,
+                                 g_one_launch_mode.load(std::memory_order_relaxed), &w.one_launch);
     if (w.step.sel_rep > 0) {
       w.plan = fsa::AttnPlan{0, 0};
       w.slots = w.step.pw.wg_per_unit + w.step.sel_rep;
@@ -421,7 +434,10 @@ fsa_status run_sparse_step(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_sca
                                       at<float>(workspace, w.part_ml), out);
     return hip_status(fsa::launch_attention(fsa::kDense, w.plan, a, st, &mk), "dense decode attention launch");
   }
-  if (mk.take())
+  // one launch for the whole step (the plain step only: the combined call's
+  // append runs inside the scoring launch)
+  const bool one = w.one && !append;
+  if (!one && mk.take())
     FSA_CHECK(hip_status(
       fsa::launch_quest_scores(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(meta),
                                fused ? append->seq_lens : seq_lens, at<float>(workspace, w.scores), dims->batch,
@@ -463,6 +479,14 @@ fsa_status run_sparse_step(const fsa_dims* dims, fsa_layer_cfg cfg, float sm_sca
   sa.by_hkv = fsa::make_fastdiv((uint32_t)dims->num_kv_heads);
   sa.by_rep = fsa::make_fastdiv((uint32_t)std::max(1, sa.sel_rep));
   sa.by_pw = fsa::make_fastdiv((uint32_t)std::max(1, sa.pw_wg));
+  sa.out = static_cast<uint16_t*>(out);
+  if (one) {
+    if (!mk.take()) return FSA_OK;
+    fsa::OneLaunchArgs o = w.one_launch;
+    o.meta = static_cast<const uint16_t*>(meta);
+    FSA_CHECK(hip_status(fsa::one_launch_slot(&o.sync), "one-launch step: synchronisation slot"));
+    return hip_status(fsa::launch_one_step(sa, o, st), "one-launch step launch");
+  }
   if (mk.take()) FSA_CHECK(hip_status(fsa::launch_select_attend(sa, st), "selection launch"));
   fsa::AttnArgs a = attn_args(dims, w.step.sel_items, sm_scale, max_seq_len, q, k_cache, v_cache, page_table, seq_lens,
                               at<int32_t>(workspace, w.sel_work), at<float>(workspace, w.part_o),
@@ -591,7 +615,7 @@ int32_t fsa_describe_step(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_s
     return -1;
   }
   const SparseWs w = sparse_ws(dims, cfg, max_seq_len);
-  const int32_t v[9] = {w.all_taken ? 0 : (w.step.sel_rep > 0 ? 1 : 2),
+  const int32_t v[11] = {w.all_taken ? 0 : (w.step.sel_rep > 0 ? 1 : 2),
                         w.step.sel_rep,
                         w.step.sel_rep > 0 ? w.step.per : 0,
                         w.step.xcd_grouped,
@@ -599,13 +623,25 @@ int32_t fsa_describe_step(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_s
                         w.all_taken ? 0 : w.step.pw.wg_per_unit,
                         w.slots,
                         fsa::select_columns(max_seq_len),
-                        w.all_taken ? 0 : w.step.pw.ipw};
-  const int32_t n = std::min<int32_t>(n_info, 9);
+                        w.all_taken ? 0 : w.step.pw.ipw,
+                        w.one ? 1 : 0,
+                        w.one ? w.one_launch.n_score : 0};
+  const int32_t n = std::min<int32_t>(n_info, 11);
   for (int32_t i = 0; i < n; ++i) info[i] = v[i];
   return n;
 }
 
 int32_t fsa_build_flags(void) { return fsa::kBuildFlags; }
+
+int32_t fsa_set_one_launch(int32_t mode) { return g_one_launch_mode.exchange(std::min(2, std::max(0, mode))); }
+
+fsa_status fsa_one_launch_stalls(int64_t* n) {
+  FSA_CHECK(need(n, "n"));
+  long long v = 0;
+  FSA_CHECK(hip_status(fsa::one_launch_stalls(&v), "one-launch stall count"));
+  *n = v;
+  return FSA_OK;
+}
 
 int32_t fsa_device_memory(int32_t* info, int32_t n_info) {
   if (!info || n_info < 0) {

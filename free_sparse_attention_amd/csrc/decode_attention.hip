@@ -16,6 +16,7 @@
 #include <atomic>
 
 #include "attend_core.h"
+#include "combine_core.h"
 
 namespace fsa {
 namespace {
@@ -80,24 +81,17 @@ __global__ __launch_bounds__(256, 3) void decode_attention_kernel(
                              part_ml + 2 * slot * G);
 }
 
-// One workgroup per (sequence, KV head, query head of the group): merges the
-// unit's partials for that head.  Units handled by a single workgroup were
-// finished by the attention kernel.  Thread (part, c) owns float4 column c and
-// merges every PARTS-th partial online -- running maximum, rescaled sums -- so
-// each partial's (m, l) and column are loaded together in one round trip; the
-// PARTS states of a column are then merged through LDS.
+// The combine of the decode step: one 256-thread workgroup per (unit, query
+// head) merges the unit's partials (combine_core.h); for the dense baseline,
+// units whose attention fitted one workgroup were written directly and are
+// skipped.
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, uint16_t* __restrict__ out, int hq, int hkv, int per_wg, int slots_per_unit,
     int max_seq_len, FastDiv by_g, FastDiv by_hkv) {
-  constexpr int NQ = D / 4;        // float4 columns of one head
-  constexpr int PARTS = 256 / NQ;  // threads sharing a column, each with every PARTS-th partial
-  __shared__ float sh_m[PARTS][NQ], sh_l[PARTS][NQ];
-  __shared__ float4 sh_acc[PARTS][NQ];
-  poison_lds(sh_m, sizeof(sh_m));
-  poison_lds(sh_l, sizeof(sh_l));
-  poison_lds(sh_acc, sizeof(sh_acc));
+  __shared__ CombineLds<D> S;
+  poison_lds(&S, sizeof(S));
   const int G = (int)by_g.d;
   const int unit = (int)fdiv(blockIdx.x, by_g), h = (int)blockIdx.x - unit * G;
   const int b = (int)fdiv((uint32_t)unit, by_hkv), g = unit - b * hkv;
@@ -109,54 +103,19 @@ __global__ __launch_bounds__(256) void combine_kernel(
     n = ((L + kPage - 1) / kPage + per_wg - 1) / per_wg;
   }
   if (MODE == kDense && n <= 1) return;  // written directly by the attention kernel
-  const int tid = threadIdx.x, c4 = tid % NQ, part = tid / NQ;
-  const float* ml = part_ml + 2 * ((size_t)unit * slots_per_unit * G + h);
-  const float4* po = reinterpret_cast<const float4*>(part_o + ((size_t)unit * slots_per_unit * G + h) * D) + c4;
-  const size_t wstride = (size_t)G * NQ;  // float4s between consecutive partials
-
-  float M = -INFINITY, Lsum = 0.f;
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-  for (int w = part; w < n; w += PARTS) {
-    const float m = ml[2 * (size_t)w * G];
-    const float l = ml[2 * (size_t)w * G + 1];
-    const float4 v = po[(size_t)w * wstride];
-    const float Mn = fmaxf(M, m);
-    const float ea = M == -INFINITY ? 0.f : exp2f(M - Mn);
-    const float eb = m == -INFINITY ? 0.f : exp2f(m - Mn);
-    a.x = a.x * ea + v.x * eb;
-    a.y = a.y * ea + v.y * eb;
-    a.z = a.z * ea + v.z * eb;
-    a.w = a.w * ea + v.w * eb;
-    Lsum = Lsum * ea + l * eb;
-    M = Mn;
+  const size_t first = (size_t)unit * slots_per_unit * G + h;  // the head's first partial
+  const float* ml = part_ml + 2 * first;
+  const float4* po = reinterpret_cast<const float4*>(part_o + first * D);
+  if (n <= kStrandMax * CombineLds<D>::PARTS) {  // all loads in flight at once
+    StrandLoads<D> L;
+    strand_load<D>(L, ml, po, G, n, (int)threadIdx.x);
+    strand_merge<D>(S, L, n, (int)threadIdx.x);
+  } else {
+    combine_strands<D>(S, ml, po, G, n, (int)threadIdx.x);
   }
-  sh_m[part][c4] = M;
-  sh_l[part][c4] = Lsum;
-  sh_acc[part][c4] = a;
   __syncthreads();
-  if (part == 0) {
-    float Mt = M;
-#pragma unroll
-    for (int p = 1; p < PARTS; ++p) Mt = fmaxf(Mt, sh_m[p][c4]);
-    float Lt = 0.f;
-    float4 at = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int p = 0; p < PARTS; ++p) {
-      const float mp = sh_m[p][c4];
-      const float e = mp == -INFINITY ? 0.f : exp2f(mp - Mt);
-      const float4 v = sh_acc[p][c4];
-      at.x += e * v.x;
-      at.y += e * v.y;
-      at.z += e * v.z;
-      at.w += e * v.w;
-      Lt += e * sh_l[p][c4];
-    }
-    const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;
-    const uint32_t w0 = f32_to_bf16_bits(at.x * inv) | (f32_to_bf16_bits(at.y * inv) << 16);
-    const uint32_t w1 = f32_to_bf16_bits(at.z * inv) | (f32_to_bf16_bits(at.w * inv) << 16);
-    *reinterpret_cast<uint2*>(out + ((size_t)b * hq + (size_t)g * G + h) * D + 4 * c4) = make_uint2(w0, w1);
-  }
+  if ((int)threadIdx.x < CombineLds<D>::NQ)
+    combine_write<D>(S, (int)threadIdx.x, out + ((size_t)b * hq + (size_t)g * G + h) * D);
 }
 
 }  // namespace

@@ -233,6 +233,7 @@ struct StepArgs {
   float scale_log2;
   int G;                          // hq / hkv
   FastDiv by_hkv, by_rep, by_pw;  // divisions by hkv, sel_rep (or 1), pw_wg (or 1)
+  uint16_t* out;                  // [B][Hq][D]: written by the one-launch step's merge
 };
 
 // Prefix/window attention plan: at most max_items items per unit, ipw per wave,
@@ -255,6 +256,34 @@ struct StepPlan {
 };
 StepPlan plan_step(int units, int head_dim, int prefix, int window, int budget, int max_seq_len);
 hipError_t launch_select_attend(const StepArgs& a, hipStream_t stream);
+
+// One-launch step (wide plan on a device of kXcds XCDs of 32 CUs): a single
+// launch runs the scoring, the selection replicas, the prefix/window
+// attention and the merge of the partials as tasks, taken in order from one
+// queue per XCD; the units of XCD x (units x, x + 8, ...) have all their tasks
+// on that XCD, so what one task leaves for another is in the XCD's L2.
+constexpr int kOneMaxUnits = 64;  // units of a one-launch step, at most
+constexpr int kSyncSlots = 32;    // one-launch steps in flight on one GPU, at most
+struct OneLaunchArgs {
+  void* sync;            // this step's synchronisation slot (device memory of the library)
+  const uint16_t* meta;  // the page metadata the scoring tasks read
+  int units;
+  int n_score;        // scoring tasks per unit (16 waves each)
+  int score_tpw;      // 16-page tiles per scoring wave, at most
+  FastDiv by_score;   // division by n_score
+};
+// Whether the one-launch step applies (the wide plan, at most kOneMaxUnits
+// units, at most 16 query heads per KV head and few partials per unit, a
+// device of kXcds XCDs of 32 CUs; mode 1: also a unit count that is a multiple
+// of kXcds, mode 2: any; mode 0: never), and its task sizes.
+bool plan_one_launch(const StepPlan& p, int units, int head_dim, int G, int prefix, int window, int max_seq_len,
+                     int mode, OneLaunchArgs* o);
+// Device address of the next synchronisation slot on the current device.
+hipError_t one_launch_slot(void** slot);
+hipError_t launch_one_step(const StepArgs& a, const OneLaunchArgs& o, hipStream_t stream);
+// Waits the one-launch kernel gave up on (bounded waits), summed over the
+// slots of the current device; synchronises the device (measurement and tests).
+hipError_t one_launch_stalls(long long* n);
 
 // Attention work-item sources: every page of the sequence, or the selection's work list.
 enum AttnMode { kDense = 0, kList = 1 };

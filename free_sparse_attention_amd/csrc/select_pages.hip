@@ -19,8 +19,12 @@
 //     selected items one selection workgroup per unit writes.
 // The combine merges all partials of a unit.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "attend_core.h"
+#include "combine_core.h"
+#include "score_core.h"
 #include "select_core.h"
 
 namespace fsa {
@@ -242,6 +246,203 @@ __global__ __launch_bounds__(kSelThreads) void select_attend_kernel(const StepAr
   }
 }
 
+// ---------------------------------------------------------------- one-launch step
+// The separate launches pay a launch boundary between scoring and selection
+// and another before the combine.  The one-launch step runs the whole step as
+// tasks of one launch:
+//   * each 1024-thread workgroup takes the next task from the queue of the
+//     XCD it runs on (the XCC_ID hardware register) and runs it; the grid
+//     holds eight times the longest queue (the dispatcher deals workgroups
+//     to the XCDs in turn), one workgroup per CU at a time (LDS);
+//   * XCD x serves units x, x + 8, ...; its queue holds the scoring tasks of
+//     its units (n_score per unit, 16 waves each with a share of the unit's
+//     16-page tiles; together at most one per CU of the XCD), then their
+//     selection replicas, then their prefix/window tasks;
+//   * a scoring task stores its scores, waits until the stores have
+//     completed (they are then in the XCD's L2, which every CU of the XCD
+//     reads), then adds one to its unit's score counter; a selection replica
+//     waits until that counter reaches n_score;
+//   * every selection and prefix/window task writes one partial the same way
+//     and adds one to its unit's partial counter; the task that brings it to
+//     the unit's slot count merges the unit's partials into the output with
+//     the combine's arithmetic (combine_core.h), so no combine launch is
+//     needed and the output is bit-identical to the separate launches';
+//   * every wait is on tasks earlier in the same queue, which were taken by
+//     workgroups already running that wait on nothing themselves, so the
+//     waits end whatever the order and number of resident workgroups.  One
+//     task per workgroup also keeps the roles' per-lane values out of a loop,
+//     where the compiler would hoist and spill them;
+//   * the counters are device-scope atomics in a slot of library memory (one
+//     slot per step in flight); the last workgroup to leave zeroes them for
+//     the slot's next step.
+// A wait is bounded: after about a second it is counted in the slot's stall
+// word (one_launch_stalls) and given up, so a broken assumption shows up as a
+// wrong result and a count, never as a hang.  Tasks left in a queue (an XCD
+// given fewer workgroups than its queue holds) are counted the same way by
+// the last workgroup.
+// On MI355X this form measured slower than the separate launches at every
+// length from 4k to 256k tokens (it is off unless asked for): a handoff
+// through device memory (stores completed, a device-scope atomic, a poll)
+// costs about as much as the launch boundary it replaces, the merge of the
+// partials takes about as long as the combine launch, and scoring with each
+// unit on one XCD ends later than scoring spread over every XCD, since the
+// XCDs stream at different rates.
+struct alignas(256) SyncWord {
+  uint32_t v;
+  uint32_t pad[63];
+};
+struct SyncSlot {
+  SyncWord claim[kXcds];           // tasks taken from each XCD's queue
+  SyncWord scored[kOneMaxUnits];   // scoring tasks finished, per unit
+  SyncWord arrived[kOneMaxUnits];  // partials written, per unit
+  SyncWord finished;               // workgroups of the launch that have left
+  SyncWord stalls;                 // waits given up (never reset)
+};
+// Zero when the library is loaded; every one-launch step leaves its slot zero.
+__device__ SyncSlot g_sync[kSyncSlots];
+
+constexpr uint32_t kMaxPolls = 1u << 22;  // ~1 s of polling
+
+__device__ __forceinline__ uint32_t this_xcd() {
+  return (uint32_t)__builtin_amdgcn_s_getreg((15 << 11) | 20) & 0xFu;  // HW_REG_XCC_ID, bits 0..15
+}
+__device__ __forceinline__ uint32_t sync_add(SyncWord& w, uint32_t v) {
+  return __hip_atomic_fetch_add(&w.v, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t sync_load(SyncWord& w) {
+  return __hip_atomic_load(&w.v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void sync_store(SyncWord& w, uint32_t v) {
+  __hip_atomic_store(&w.v, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Units x, x + 8, ... below `units` (none for an XCD id the plan does not know).
+__device__ __forceinline__ int xcd_units(uint32_t x, int units) {
+  return x < (uint32_t)kXcds && (int)x < units ? (units - 1 - (int)x) / kXcds + 1 : 0;
+}
+// The workgroup's stores have completed (so they are in the XCD's L2) before
+// thread 0 adds `v` to `w`; returns the old value to every thread.
+__device__ __forceinline__ uint32_t publish(SyncWord& w, uint32_t v, uint32_t* s_word) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) *s_word = sync_add(w, v);
+  __syncthreads();
+  return *s_word;
+}
+
+// The unit's partials merged into its G output rows (combine_core.h): 256
+// threads per head, four heads side by side, each thread taking heads grp,
+// grp + 4, ... (G <= kOneMaxG) with all of their loads in flight at once.
+constexpr int kOneMaxG = 16;
+template <int D>
+__device__ __forceinline__ void merge_unit(CombineLds<D> (&S)[kOneMaxG], const StepArgs& A, int unit) {
+  const int b = (int)fdiv((uint32_t)unit, A.by_hkv), g = unit - b * A.hkv, G = A.G, n = A.slots_per_unit;
+  const int grp = threadIdx.x / kCombineThreads, t = threadIdx.x % kCombineThreads;
+  constexpr int HPT = kOneMaxG / 4;  // heads per thread, at most
+  StrandLoads<D> L[HPT];
+#pragma unroll
+  for (int i = 0; i < HPT; ++i) {
+    const int h = grp + 4 * i;
+    const size_t first = (size_t)unit * n * G + h;  // the head's first partial
+    if (h < G)
+      strand_load<D>(L[i], A.part_ml + 2 * first, reinterpret_cast<const float4*>(A.part_o + first * D), G, n, t);
+  }
+#pragma unroll
+  for (int i = 0; i < HPT; ++i)
+    if (grp + 4 * i < G) strand_merge<D>(S[grp + 4 * i], L[i], n, t);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < HPT; ++i) {
+    const int h = grp + 4 * i;
+    if (h < G && t < CombineLds<D>::NQ)
+      combine_write<D>(S[h], t, A.out + ((size_t)b * A.hq + (size_t)g * G + h) * D);
+  }
+}
+
+template <int COLS, int D>
+__global__ __launch_bounds__(kSelThreads) void one_launch_step_kernel(const StepArgs A, const OneLaunchArgs O) {
+  __shared__ union {
+    SelectLds sel;
+    MergeLds<D, kSelWaves> att;
+    CombineLds<D> comb[kOneMaxG];
+  } U;
+  __shared__ int4 slice[kSliceMax];
+  __shared__ bf16x8_t q_lds[D / 32 * kWave];
+  __shared__ uint32_t s_word;
+  poison_lds(&U, sizeof(U));
+  poison_lds(slice, sizeof(slice));
+  poison_lds(q_lds, sizeof(q_lds));
+  SyncSlot& S = *static_cast<SyncSlot*>(O.sync);
+  const int wave = threadIdx.x >> 6;
+  const uint32_t x = this_xcd();
+  const int nu = xcd_units(x, O.units);
+  const int n_sc = nu * O.n_score;           // scoring tasks
+  const int n_sel = n_sc + nu * A.sel_rep;  // + selection replicas
+  const int n_tasks = n_sel + nu * A.pw_wg;  // + prefix/window tasks
+  if (threadIdx.x == 0) s_word = nu > 0 ? sync_add(S.claim[x], 1u) : (uint32_t)n_tasks;
+  __syncthreads();
+  const int t = (int)s_word;
+  if (t < n_sc) {
+    const int k = (int)fdiv((uint32_t)t, O.by_score), r = t - k * O.n_score;
+    const int unit = (int)x + kXcds * k;
+    const int b = (int)fdiv((uint32_t)unit, A.by_hkv), g = unit - b * A.hkv;
+    const ScoreArgs SA{A.q, O.meta, A.seq_lens, const_cast<float*>(A.scores), A.hq, A.hkv, A.max_pages,
+                       A.prefix, A.window, A.max_seq_len, 0, A.G};
+    score_wave<D>(SA, unit, b, g, r * kSelWaves + wave, O.n_score * kSelWaves, O.score_tpw);
+    publish(S.scored[unit], 1u, &s_word);
+  } else if (t < n_tasks) {
+    int unit;
+    if (t < n_sel) {
+      const int k = (int)fdiv((uint32_t)(t - n_sc), A.by_rep), r = t - n_sc - k * A.sel_rep;
+      unit = (int)x + kXcds * k;
+      if (threadIdx.x == 0) {
+        uint32_t polls = 0;
+        while (sync_load(S.scored[unit]) < (uint32_t)O.n_score) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++polls == kMaxPolls) {
+            sync_add(S.stalls, 1u);
+            break;
+          }
+        }
+      }
+      __syncthreads();
+      select_and_attend<COLS, D>(U.sel, U.att, slice, q_lds, A, unit, r);
+    } else {
+      const int w = t - n_sel;
+      const int k = (int)fdiv((uint32_t)w, A.by_pw);
+      unit = (int)x + kXcds * k;
+      prefix_window_attend<D>(U.att, A, unit, w - k * A.pw_wg);
+    }
+    // the task that writes the unit's last partial merges them all (the
+    // partials are in this XCD's L2; this CU has read none of them before)
+    if (publish(S.arrived[unit], 1u, &s_word) == (uint32_t)A.slots_per_unit - 1) {
+      poison_lds(&U, sizeof(U));
+      merge_unit<D>(U.comb, A, unit);
+    }
+  }
+  // Leaving: `finished` counts workgroups in its low 16 bits and tasks run in
+  // its high bits.  The last workgroup checks that every task ran (an XCD
+  // given fewer workgroups than its queue holds leaves some undone) and zeroes
+  // the slot for its next step, one word per thread.
+  if (threadIdx.x == 0) {
+    const uint32_t add = 1u + (t < n_tasks ? 1u << 16 : 0u);
+    const uint32_t now = sync_add(S.finished, add) + add;
+    s_word = (now & 0xFFFFu) == gridDim.x ? now >> 16 : 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  const uint32_t ran = s_word;
+  if (ran != 0xFFFFFFFFu) {
+    const int i = threadIdx.x;
+    if (i == 0 && ran != (uint32_t)(O.units * (O.n_score + A.sel_rep + A.pw_wg))) sync_add(S.stalls, 1u);
+    if (i < kXcds) sync_store(S.claim[i], 0u);
+    if (i < O.units) {
+      sync_store(S.scored[i], 0u);
+      sync_store(S.arrived[i], 0u);
+    }
+    if (i == 0) sync_store(S.finished, 0u);
+  }
+}
+
 }  // namespace
 
 int select_max_candidates() { return kSelMaxPages; }
@@ -346,6 +547,102 @@ hipError_t launch_select_attend(const StepArgs& a, hipStream_t stream) {
   }
 #undef FSA_SA_D
 #undef FSA_SA
+  return hipGetLastError();
+}
+
+bool plan_one_launch(const StepPlan& p, int units, int head_dim, int G, int prefix, int window, int max_seq_len,
+                     int mode, OneLaunchArgs* o) {
+  const int cus = device_cu_count();
+  if (mode == 0 || p.sel_rep <= 0 || units > kOneMaxUnits || cus != kXcds * 32) return false;
+  // the in-launch merge: every head's partials loaded at once
+  const int parts = kCombineThreads / (head_dim / 4);
+  if (G > kOneMaxG || p.sel_rep + p.pw.wg_per_unit > kStrandMax * parts) return false;
+  // automatic: only when every XCD serves as many units as the others (each
+  // unit's metadata is streamed by its own XCD)
+  if (mode == 1 && units % kXcds != 0) return false;
+  // candidate tiles at the host bound (as the scoring wave counts them); the
+  // scoring tasks of an XCD take one round of its 32 CUs at most (smaller
+  // tasks in more rounds measured slower, and so did scoring spread over all
+  // XCDs with the scores passed on through device-scope atomics)
+  const int c_lo = std::min(prefix, max_seq_len) / kPage;
+  const int c_hi = (std::max(0, max_seq_len - window) + kPage - 1) / kPage;
+  const int tiles = std::max(1, (c_hi + kMetaTile - 1) / kMetaTile - c_lo / kMetaTile);
+  const int per_xcd = (units + kXcds - 1) / kXcds;
+  o->units = units;
+  o->n_score = std::max(1, std::min((tiles + kSelWaves - 1) / kSelWaves, 32 / per_xcd));
+  o->score_tpw = (tiles + kSelWaves * o->n_score - 1) / (kSelWaves * o->n_score);
+  o->by_score = make_fastdiv((uint32_t)o->n_score);
+  return true;
+}
+
+namespace {
+constexpr int kMaxSyncDevices = 64;
+std::mutex g_sync_mu;
+SyncSlot* g_sync_ptr[kMaxSyncDevices] = {};
+std::atomic<unsigned> g_sync_next{0};
+}  // namespace
+
+hipError_t one_launch_slot(void** slot) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxSyncDevices) return hipErrorInvalidDevice;
+  SyncSlot* base = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_sync_mu);
+    if (!g_sync_ptr[dev]) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_sync));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_sync_ptr[dev] = static_cast<SyncSlot*>(p);
+    }
+    base = g_sync_ptr[dev];
+  }
+  *slot = base + g_sync_next.fetch_add(1, std::memory_order_relaxed) % kSyncSlots;
+  return hipSuccess;
+}
+
+hipError_t one_launch_stalls(long long* n) {
+  void* p = nullptr;
+  hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_sync));
+  if (e != hipSuccess) return e;
+  e = hipDeviceSynchronize();
+  if (e != hipSuccess) return e;
+  long long sum = 0;
+  for (int i = 0; i < kSyncSlots; ++i) {
+    uint32_t v = 0;
+    e = hipMemcpy(&v, &static_cast<SyncSlot*>(p)[i].stalls.v, sizeof(v), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return e;
+    sum += v;
+  }
+  *n = sum;
+  return hipSuccess;
+}
+
+hipError_t launch_one_step(const StepArgs& a, const OneLaunchArgs& o, hipStream_t stream) {
+  // one task per workgroup: eight times the longest XCD queue
+  const int per_xcd = (o.units + kXcds - 1) / kXcds * (o.n_score + a.sel_rep + a.pw_wg);
+  const unsigned grid = (unsigned)(kXcds * per_xcd);
+#define FSA_ONE(C, DD) \
+  hipLaunchKernelGGL((one_launch_step_kernel<C, DD>), dim3(grid), dim3(kSelThreads), 0, stream, a, o)
+#define FSA_ONE_D(C)        \
+  do {                      \
+    if (a.d == 128)         \
+      FSA_ONE(C, 128);      \
+    else                    \
+      FSA_ONE(C, 64);       \
+  } while (0)
+  switch (select_cols(a.max_seq_len)) {
+    case 1: FSA_ONE_D(1); break;
+    case 2: FSA_ONE_D(2); break;
+    case 4: FSA_ONE_D(4); break;
+    case 8: FSA_ONE_D(8); break;
+    case 16: FSA_ONE_D(16); break;
+    default: FSA_ONE_D(32); break;
+  }
+#undef FSA_ONE_D
+#undef FSA_ONE
   return hipGetLastError();
 }
 

@@ -246,6 +246,11 @@ fsa_status fsa_sparse_decode_attn_noalloc(const fsa_dims* dims, fsa_layer_cfg cf
  *   info[7]  pages per selection thread (a power of two)
  *   info[8]  prefix/window items each wave of a prefix/window workgroup
  *            attends (16 waves per workgroup)
+ *   info[9]  1 if the wide plan runs as one launch (scoring, selection,
+ *            prefix/window attention and the merge of the partials as tasks
+ *            of one launch, each unit's tasks on one XCD); the call with an
+ *            append (fsa_append_decode_attn) keeps the separate launches
+ *   info[10] scoring tasks per unit in that launch, else 0
  * Returns the number of entries written, or -1 with fsa_last_error() set. */
 int32_t fsa_describe_step(const fsa_dims* dims, fsa_layer_cfg cfg, int32_t max_seq_len, int32_t* info,
                           int32_t n_info);

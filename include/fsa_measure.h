@@ -37,12 +37,28 @@ fsa_status fsa_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* s
  * only, no device needed. */
 int32_t fsa_build_flags(void);
 
+/* When later calls in this process use the one-launch form of the wide plan
+ * (fsa_describe_step info[9]), so that both forms can be timed and checked on
+ * the same inputs: mode 0 never (the default), 1 where it applies and the
+ * (sequence, KV head) units are a multiple of 8 (each unit's tasks run on one
+ * of the 8 XCDs), 2 wherever it applies (any unit count up to 64).  Other
+ * values are clamped to 0..2.  Returns the previous mode.  Host only. */
+int32_t fsa_set_one_launch(int32_t mode);
+
+/* Waits that one-launch steps on the current device gave up on, summed since
+ * the library was loaded: each wait of the one-launch kernel for another
+ * task is bounded (about a second), and a step whose queues were not all
+ * emptied counts one too.  Nonzero means a step's result is wrong.
+ * Synchronises the device.  FSA_ERR_HIP on a failed device call. */
+fsa_status fsa_one_launch_stalls(int64_t* n);
+
 /* Some of the launches of the fsa_sparse_decode_attn step, so that parts of
  * the step can be timed: runs only launches first..last (0-based, inclusive)
  * of the step these arguments describe.  The launches, in order: dense plan
  * -- [selection, when sel_pages is given], split-K attention, [combine]; wide
  * plan -- scoring, selection launch (selection replicas + prefix/window
- * attention), combine; narrow plan -- scoring, selection launch, split-K
+ * attention), combine, or in its one-launch form that one launch; narrow
+ * plan -- scoring, selection launch, split-K
  * attention, combine (fsa_describe_step names the plan).  A launch reads what
  * the earlier ones left in the workspace, so when first > 0 a whole step with
  * the same arguments and workspace must have run before on the stream.

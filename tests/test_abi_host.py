@@ -298,3 +298,30 @@ int main() {
     assert r.returncode == 0, r.stderr[-2000:]
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert out.returncode == 0 and out.stdout.strip() == "0", (out.stdout, out.stderr[-500:])
+
+
+def test_one_launch_plan_modes(lib):
+    """The one-launch form of the wide plan (on 256 CUs, the count assumed
+    without a device): off by default; mode 1 for unit counts that are
+    multiples of 8 up to 64, mode 2 for any count up to 64."""
+    def plan(units, mode):
+        old = fsa.set_one_launch(mode)
+        try:
+            d = fsa.dims(units // 4, 16, 4, 128, 4096, units // 4 * 4096)
+            return fsa.describe_step(d, fsa.cfg(128, 1024, 32 if units == 64 else 128), 65536)
+        finally:
+            fsa.set_one_launch(old)
+    for units, want in ((16, 1), (64, 1), (8, 1), (12, 0), (4, 0)):
+        got = plan(units, 1)
+        assert got["plan"] == "wide" and got["one_launch"] == want, (units, got)
+        assert (got["score_tasks"] > 0) == (want == 1)
+    assert plan(12, 2)["one_launch"] == 1 and plan(4, 2)["one_launch"] == 1
+    assert plan(16, 0)["one_launch"] == 0
+    d = fsa.dims(4, 16, 4, 128, 4096, 4 * 4096)
+    assert fsa.describe_step(d, fsa.cfg(128, 1024, 128), 65536)["one_launch"] == 0  # the default
+    # scoring tasks of 16 waves, an XCD's at most one round of its 32 CUs:
+    # 65536 tokens, window 1024 -> candidate pages 8 .. 4031 in tiles 0 .. 251,
+    # 16 tasks of one tile per wave for 2 units per XCD, 4 for 8 units per XCD
+    p = plan(16, 1)
+    assert p["score_tasks"] == 16 and p["replicas"] == 8
+    assert plan(64, 1)["score_tasks"] == 4
