@@ -34,6 +34,16 @@ MALL_BYTES = 256 << 20
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
 
 
+def head_start(stream, ms):
+    """Enqueue a kernel that spins for about `ms` milliseconds on `stream`, so
+    that the launches enqueued behind it find the GPU busy (measurement of
+    GPU-side durations only; never inside a timed step region)."""
+    import torch
+    hz = 2.4e9  # MI355X's peak shader clock: at lower clocks the spin only lasts longer
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(ms * 1e-3 * hz))
+
+
 class HipEvent:
     """A HIP timing event created with flags (torch's events take none)."""
     _hip = None
@@ -278,10 +288,12 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
         fsa.sparse_decode_attn(base.dims, c, wl.sm_scale, msl, base.q, k, v, m, base.page_table, base.seq_lens,
                                out, None, ws, stream)
 
-    def timed(fn, n, w):
+    def timed(fn, n, w, lead_ms=0.0):
         for i in range(w):
             fn(i)
         torch.cuda.synchronize()
+        if lead_ms:
+            head_start(stream, lead_ms)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for i in range(n):
@@ -357,7 +369,8 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
     pre = [0.0] * len(names)
     for _ in range(rounds):
         for j in range(len(names)):
-            pre[j] += timed(prefix_fn(j), n_l // rounds, 10) / rounds
+            # (with a backlog ahead of the timed launches, as for the spans below)
+            pre[j] += timed(prefix_fn(j), n_l // rounds, 10, lead_ms=1e-3 * 40.0 * (n_l // rounds)) / rounds
     per = [pre[0]] + [max(1e-6, pre[j] - pre[j - 1]) for j in range(1, len(names))]
 
     # and each launch's own duration: every launch of at least 200 rotated
@@ -367,6 +380,10 @@ def measure(wl, steps, warmup, with_dense=True, reps_kernel=None):
     # the spans then match what a kernel trace reports per dispatch.
     def bracketed(n, w, flags):
         ev = [[(HipEvent(flags), HipEvent(flags)) for _ in names] for _ in range(n)]
+        # The host issues each launch with its two events more slowly than the
+        # GPU runs it; a spin kernel ahead of the loop gives the GPU a backlog,
+        # so that no span includes the host's enqueue gaps.
+        head_start(stream, 1e-3 * 40.0 * (n + w) * len(names))
         for i in range(w + n):
             k, v, m = reps[i % R]
             for j in range(len(names)):
