@@ -7,12 +7,14 @@ wrote shows up as NaN or garbage in the scores, selections, work lists or
 outputs.  The cases below rerun parity checks of the other GPU test modules,
 unchanged, with the binding switched to that build: every kernel and both
 step plans, the stand-alone selection, the dense path, the append, 16 and 32
-pages per selection thread, and the 64k and 256k workloads.
+pages per selection thread, the 64k and 256k workloads, and the one-launch
+form of the step against the separate launches.
 """
 import os
 
 import pytest
 
+import tests.test_gpu_one_launch as O
 import tests.test_gpu_parity as P
 import tests.test_gpu_workloads as W
 from free_sparse_attention_amd import _lib
@@ -33,6 +35,8 @@ CASES = [
     (P.test_append_matches_rebuild_and_oracle, {}),
     (W.test_ctx64k_all_units, {}),
     (W.test_ctx256k_all_units, {}),
+    (O.test_one_launch_equals_separate_launches, {"case": "b4_h4_ragged"}),
+    (O.test_one_launch_equals_separate_launches, {"case": "b3_h2_d64"}),
 ]
 
 
