@@ -9,9 +9,11 @@ of the KV cache and metadata (the situation of successive full-attention
 layers, each with its own cache), with R x the bytes a step reads >= 2 x 256 MB.
 
 Prints one JSON line.  Default workload: batch-4 decode at 64k context
-(Hq 16 / Hkv 4, D 128, prefix 128, window 1024, budget 128 pages); the 256k
-workload (Hq 32 / Hkv 4, permuted pool, prefix 128, window 4096, budget 256)
-is measured too and reported under "also".
+(Hq 16 / Hkv 4, D 128, prefix 128, window 1024, budget 128 pages).  Reported
+under "also": the 256k workload (Hq 32 / Hkv 4, permuted pool, prefix 128,
+window 4096, budget 256), the 16-sequence ragged serving step (append +
+decode) and the 12-layer model step at 128k (append + decode per layer, each
+layer with its own cache and prefix/window/budget).
 """
 from __future__ import annotations
 
@@ -702,7 +704,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="ctx64k", help="tiny, ctx64k or ctx256k")
-    ap.add_argument("--no-also", action="store_true", help="skip the 256k and ragged serving measurements")
+    ap.add_argument("--no-also", action="store_true",
+                    help="skip the 256k, ragged serving and 12-layer measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--sweep", action="store_true",
@@ -783,6 +786,8 @@ def main():
     if not args.no_also:
         log("[bench] ragged16 serving step")
         also["ragged16"] = ragged_serving(max(20, args.steps // 4), 4)
+        log("[bench] layers12 model step")
+        also["layers12"] = layers12(max(10, args.steps // 10), 4)
 
     r = main_res
     top = max(r["launches"], key=lambda x: x["avg_launch_us"])
@@ -816,7 +821,14 @@ def main():
         "detail": {k: v for k, v in r.items()},
     }
     for k, v in also.items():
-        if k == "ragged16":
+        if k == "layers12":
+            line["also"][k] = {"us_per_model_step": v["eager_us_per_model_step"],
+                               "us_per_layer": v["eager_us_per_layer"],
+                               "graph_us_per_model_step": v["graph_us_per_model_step"],
+                               "separate_calls_us_per_model_step": v["separate_calls_eager_us_per_model_step"],
+                               "step": "12 layers at 128k, each a one-token append + sparse decode (own cache, "
+                                       "per-layer prefix/window/budget)", "detail": v}
+        elif k == "ragged16":
             line["also"][k] = {"steps_per_s": v["steps_per_s"], "us_per_step": v["us_per_step"],
                                "achieved_GBps": v["step_GBps"], "pct_hbm_peak": 100.0 * v["step_GBps"] / HBM_PEAK_GBS,
                                "speedup_vs_dense": v["speedup_vs_dense"], "step": "one-token append + sparse decode",
