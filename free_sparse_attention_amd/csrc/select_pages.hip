@@ -571,6 +571,8 @@ bool plan_one_launch(const StepPlan& p, int units, int head_dim, int G, int pref
   o->units = units;
   o->n_score = std::max(1, std::min((tiles + kSelWaves - 1) / kSelWaves, 32 / per_xcd));
   o->score_tpw = (tiles + kSelWaves * o->n_score - 1) / (kSelWaves * o->n_score);
+  // the kernel counts its workgroups in 16 bits
+  if ((long)kXcds * per_xcd * (o->n_score + p.sel_rep + p.pw.wg_per_unit) >= 0x10000) return false;
   o->by_score = make_fastdiv((uint32_t)o->n_score);
   return true;
 }
