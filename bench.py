@@ -442,7 +442,8 @@ SWEEP_LENS = (2048, 4096, 8192, 16384, 32768, 65536, 131072, 262144, 524288)
 
 def crossover_sweep(steps, warmup):
     """Sparse and dense step times at the 64k workload's shapes (batch 4, Hq 16 / Hkv 4,
-    D 128, prefix 128, window 1024, budget 128 pages) for context lengths 2k..512k."""
+    D 128, prefix 128, window 1024, budget 128 pages) for context lengths 2k..512k,
+    with the sparse step also in its one-launch form where that applies."""
     import synth
     import torch
     # bring the clocks up before the first (shortest, latency-bound) point
@@ -462,7 +463,8 @@ def crossover_sweep(steps, warmup):
         rows.append({"seq_len": L, "candidate_pages": C,
                      "path": "dense (every candidate fits the budget)" if C <= budget else "sparse",
                      "sparse_us": 1000.0 * r["ms_per_step"], "dense_us": 1000.0 * r["dense_ms_per_step"],
-                     "speedup_vs_dense": r["speedup_vs_dense"], "step_GBps": r["step_GBps"]})
+                     "speedup_vs_dense": r["speedup_vs_dense"], "step_GBps": r["step_GBps"],
+                     "one_launch_us": r["one_launch_step_us"]})
         log(f"[sweep] L={L}: sparse {rows[-1]['sparse_us']:.1f} us, dense {rows[-1]['dense_us']:.1f} us")
         del wl
     return rows

@@ -158,9 +158,9 @@ struct SparseWs {
 };
 
 // When the one-launch form of the wide plan is used (fsa_set_one_launch): 0
-// never (the default: it measured slower than the separate launches at 4k to
-// 256k tokens), 1 where it applies and the units spread evenly over the XCDs,
-// 2 wherever it applies.
+// never (the default: it measured no faster than the separate launches from
+// 4k to 512k tokens, and slower at 64k and 256k), 1 where it applies and the
+// units spread evenly over the XCDs, 2 wherever it applies.
 std::atomic<int> g_one_launch_mode{0};
 
 SparseWs sparse_ws(const fsa_dims* d, fsa_layer_cfg c, int32_t max_seq_len) {

@@ -280,8 +280,9 @@ __global__ __launch_bounds__(kSelThreads) void select_attend_kernel(const StepAr
 // wrong result and a count, never as a hang.  Tasks left in a queue (an XCD
 // given fewer workgroups than its queue holds) are counted the same way by
 // the last workgroup.
-// On MI355X this form measured slower than the separate launches at every
-// length from 4k to 256k tokens (it is off unless asked for): a handoff
+// On MI355X this form measured no faster than the separate launches from 4k
+// to 512k tokens (within half a microsecond at the shortest and longest
+// lengths, up to 2 us slower in between), so it is off unless asked for: a handoff
 // through device memory (stores completed, a device-scope atomic, a poll)
 // costs about as much as the launch boundary it replaces, the merge of the
 // partials takes about as long as the combine launch, and scoring with each
