@@ -33,11 +33,14 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     fsa.load()
+    yield
+    fsa.set_one_launch(0)
+
+
+def _need_256_cus():
     cus = fsa.device_memory()["compute_units"]
     if cus != 256:  # the one-launch form needs 8 XCDs of 32 CUs (MI355X as one partition)
         pytest.skip(f"the one-launch form needs a 256-CU device, this one has {cus}")
-    yield
-    fsa.set_one_launch(0)
 
 
 # (workload, overrides): units below, at and above one per XCD; G 4, 8 and 1;
@@ -68,6 +71,7 @@ def _both(dw, cfg=None):
 
 @pytest.mark.parametrize("case", list(CASES))
 def test_one_launch_equals_separate_launches(case):
+    _need_256_cus()
     name, over = CASES[case]
     wl = synth.make_workload(name, **over)
     dw = DeviceWorkload(wl)
@@ -83,6 +87,7 @@ def test_one_launch_equals_separate_launches(case):
 
 
 def test_slots_reused_graph_replays_and_launches_one_at_a_time():
+    _need_256_cus()
     wl = synth.make_workload("ctx64k", seq_lens=(12000, 15000, 9000, 20000))
     dw = DeviceWorkload(wl)
     before = fsa.one_launch_stalls()
